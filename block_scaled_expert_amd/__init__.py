@@ -1,0 +1,223 @@
+"""Python binding of libmoe.so, the gfx950 routed-expert MoE library.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels on the caller's current torch stream.  The functions mirror the C
+ABI in include/moe.h (moe_route, moe_dispatch, moe_quantize_act,
+moe_forward, moe_workspace_size, moe_check_arch, moe_status_string).
+Tensors must be contiguous and on the current CUDA (HIP) device; the library
+never allocates, so callers pass outputs and a workspace.
+
+There is no fallback: if the built library is missing, load() raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+FMT_NVFP4, FMT_MXFP8 = 1, 2
+FMTS = {"nvfp4": FMT_NVFP4, "mxfp8": FMT_MXFP8}
+CAP_SOFT_GATE_UP, CAP_HARD_GATE_UP, CAP_SOFT_OUT, CAP_NONE = 0, 1, 2, 3
+DTYPE_BF16, DTYPE_F32 = 0, 1
+STAGES = ("quant_x", "dispatch", "gate_up", "quant_h", "down", "combine")
+
+EXPORTED = ("moe_status_string", "moe_check_arch", "moe_validate_config", "moe_workspace_size",
+            "moe_quantize_act", "moe_route", "moe_dispatch", "moe_forward")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class CConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("expert_begin", ctypes.c_int32),
+                ("num_local_experts", ctypes.c_int32), ("fmt", ctypes.c_int32), ("cap_form", ctypes.c_int32),
+                ("cap", ctypes.c_float), ("norm_topk", ctypes.c_int32), ("routed_scale", ctypes.c_float),
+                ("max_tokens", ctypes.c_int32)]
+
+
+class CWeights(ctypes.Structure):
+    _fields_ = [("w13", ctypes.c_void_p), ("w13_sc", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w2_sc", ctypes.c_void_p), ("gs", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmoe.so (built by block_scaled_expert_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m block_scaled_expert_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_check_arch.argtypes = [ctypes.c_char_p]
+    lib.moe_validate_config.argtypes = [ctypes.POINTER(CConfig)]
+    lib.moe_workspace_size.argtypes = [ctypes.POINTER(CConfig), ctypes.POINTER(sz)]
+    lib.moe_quantize_act.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp]
+    lib.moe_route.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_dispatch.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_forward.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, ctypes.POINTER(CWeights), vp, vp,
+                                sz, vp, vp]
+    for name in EXPORTED:
+        if name != "moe_status_string":
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def check_arch(arch: str) -> int:
+    return load().moe_check_arch(arch.encode())
+
+
+@dataclass
+class Config:
+    hidden: int = 4608
+    ffn: int = 2304
+    num_experts: int = 384
+    top_k: int = 8
+    fmt: str = "nvfp4"
+    expert_begin: int = 0
+    num_local_experts: int | None = None
+    cap_form: int = CAP_SOFT_GATE_UP
+    cap: float = 7.0
+    norm_topk: bool = True
+    routed_scale: float = 1.0
+    max_tokens: int = 64
+
+    @property
+    def num_local(self) -> int:
+        return self.num_experts if self.num_local_experts is None else self.num_local_experts
+
+    def c(self) -> CConfig:
+        if self.fmt not in FMTS:
+            raise ValueError(f"unknown format {self.fmt!r}")
+        return CConfig(self.hidden, self.ffn, self.num_experts, self.top_k, self.expert_begin, self.num_local,
+                       FMTS[self.fmt], self.cap_form, self.cap, int(bool(self.norm_topk)), self.routed_scale,
+                       self.max_tokens)
+
+
+def _ok(status: int, what: str) -> None:
+    if status != 0:
+        raise MoeError(status, what)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def workspace_size(cfg: Config) -> int:
+    n = ctypes.c_size_t(0)
+    cc = cfg.c()
+    _ok(load().moe_workspace_size(ctypes.byref(cc), ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def workspace(cfg: Config, device="cuda"):
+    import torch
+    return torch.empty(workspace_size(cfg), dtype=torch.uint8, device=device)
+
+
+def quantize_act(fmt: str, x, codes, scales, row_gs=None) -> None:
+    """Per-row NVFP4 / MXFP8 quantization of a bf16 or fp32 [rows, cols] tensor."""
+    import torch
+    rows, cols = x.shape
+    dt = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}.get(x.dtype)
+    if dt is None:
+        raise ValueError("x must be bfloat16 or float32")
+    nv = fmt == "nvfp4"
+    _ptr(x, name="x")
+    args = (FMTS[fmt], dt, _ptr(x), rows, cols,
+            _ptr(codes, torch.uint8, (rows, cols // 2 if nv else cols), "codes"),
+            _ptr(scales, torch.uint8, (rows, cols // (16 if nv else 32)), "scales"),
+            _ptr(row_gs, torch.float32, (rows,), "row_gs") if nv else None, _stream())
+    _ok(load().moe_quantize_act(*args), "moe_quantize_act")
+
+
+def route(cfg: Config, x, w_router, bias, topk_ids, topk_w, near_tie, ws) -> None:
+    import torch
+    T = x.shape[0]
+    H, E, k = cfg.hidden, cfg.num_experts, cfg.top_k
+    cc = cfg.c()
+    _ok(load().moe_route(ctypes.byref(cc), _ptr(x, torch.bfloat16, (T, H), "x"), T,
+                         _ptr(w_router, torch.bfloat16, (E, H), "w_router"),
+                         _ptr(bias, torch.float32, (E,), "bias"),
+                         _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+                         _ptr(topk_w, torch.float32, (T, k), "topk_w"),
+                         _ptr(near_tie, torch.uint8, (T,), "near_tie"),
+                         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream()), "moe_route")
+
+
+def dispatch(cfg: Config, topk_ids, expert_offsets, sorted_pairs=None, pair_pos=None, ws=None) -> None:
+    import torch
+    T = topk_ids.shape[0]
+    P = T * cfg.top_k
+    cc = cfg.c()
+    _ok(load().moe_dispatch(ctypes.byref(cc), _ptr(topk_ids, torch.int32, (T, cfg.top_k), "topk_ids"), T,
+                            _ptr(expert_offsets, torch.int32, (cfg.num_local + 1,), "expert_offsets"),
+                            _ptr(sorted_pairs, torch.int32, None, "sorted_pairs"),
+                            _ptr(pair_pos, torch.int32, (P,), "pair_pos"),
+                            _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream()), "moe_dispatch")
+
+
+def weights_struct(cfg: Config, w: dict) -> CWeights:
+    """w: dict of device tensors w13, w13_sc, w2, w2_sc (uint8) and gs (fp32, NVFP4)."""
+    import torch
+    H, F, n = cfg.hidden, cfg.ffn, cfg.num_local
+    nv = cfg.fmt == "nvfp4"
+    shapes = {
+        "w13": (n, 2 * F, H // 2 if nv else H), "w13_sc": (n, 2 * F, H // (16 if nv else 32)),
+        "w2": (n, H, F // 2 if nv else F), "w2_sc": (n, H, F // (16 if nv else 32)),
+    }
+    ptrs = {k: _ptr(w[k], torch.uint8, s, k) for k, s in shapes.items()}
+    gs = _ptr(w["gs"], torch.float32, (n, 3), "gs") if nv else None
+    return CWeights(ptrs["w13"], ptrs["w13_sc"], ptrs["w2"], ptrs["w2_sc"], gs)
+
+
+def forward(cfg: Config, x, topk_ids, topk_w, weights, out, ws, events=None) -> None:
+    """weights: dict of device tensors or a CWeights built by weights_struct.
+    events: optional list of 2*6 torch.cuda.Event (stage timing)."""
+    import torch
+    T = x.shape[0]
+    H, k = cfg.hidden, cfg.top_k
+    cw = weights if isinstance(weights, CWeights) else weights_struct(cfg, weights)
+    ev = None
+    if events is not None:
+        if len(events) != 2 * len(STAGES):
+            raise ValueError("events must hold 2 per stage")
+        ev = (ctypes.c_void_p * len(events))(*[e.cuda_event if e is not None else None for e in events])
+    cc = cfg.c()
+    _ok(load().moe_forward(ctypes.byref(cc), _ptr(x, torch.bfloat16, (T, H), "x"), T,
+                           _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+                           _ptr(topk_w, torch.float32, (T, k), "topk_w"), ctypes.byref(cw),
+                           _ptr(out, torch.bfloat16, (T, H), "out"), _ptr(ws, torch.uint8, None, "ws"),
+                           ws.numel(), _stream(), ev), "moe_forward")

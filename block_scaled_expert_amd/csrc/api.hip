@@ -1,0 +1,289 @@
+// C ABI of the MoE library (include/moe.h): argument checking, the gfx950
+// check, workspace carving and the launch sequence.  Nothing here allocates,
+// frees or synchronizes; every launch goes on the caller's stream.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "launch.h"
+#include "moe_common.h"
+
+using namespace moe;
+
+namespace {
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, -1 other.
+std::atomic<int> g_arch_ok[64];
+
+int device_check() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MOE_ERR_UNSUPPORTED_DEVICE;
+  int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+    v = moe_check_arch(prop.gcnArchName) == MOE_OK ? 1 : -1;
+    g_arch_ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
+}
+
+int n_local(const moe_config* c) { return c->num_local_experts; }
+
+// Workspace regions (byte offsets, each 256-byte aligned).
+struct Layout {
+  size_t z, xq, xs, xg, counts, offsets, sorted, pos, work, ntiles, h, hq, hs, hg, y, total;
+  int max_tiles, nchunks;
+};
+
+Layout layout(const moe_config* c, int T) {
+  Layout L;
+  const size_t H = c->hidden, F = c->ffn, E = c->num_experts, EL = n_local(c), k = c->top_k;
+  const size_t P = (size_t)T * k;
+  const bool nv = c->fmt == MOE_FMT_NVFP4;
+  L.nchunks = P > 0 ? ceil_div((long)P, dispatch_chunk((int)P)) : 0;
+  L.max_tiles = ceil_div((long)P, 32) + (int)EL;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.z = take((size_t)T * E * 4);
+  L.xq = take((size_t)T * (nv ? H / 2 : H));
+  L.xs = take((size_t)T * (nv ? H / 16 : H / 32));
+  L.xg = take((size_t)T * 4);
+  // dispatch never uses more than 1024 chunks (see dispatch_chunk)
+  L.counts = take((size_t)(1024 + 1) * EL * 4);
+  L.offsets = take((EL + 1) * 4);
+  L.sorted = take(P * 4);
+  L.pos = take(P * 4);
+  L.work = take((size_t)L.max_tiles * 2 * 4);
+  L.ntiles = take(4);
+  L.h = take(P * F * 4);
+  L.hq = take(P * (nv ? F / 2 : F));
+  L.hs = take(P * (nv ? F / 16 : F / 32));
+  L.hg = take(P * 4);
+  L.y = take(P * H * 4);
+  L.total = o;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int check_ws(const moe_config* c, int T, void* ws, size_t ws_bytes) {
+  if (T > c->max_tokens) return MOE_ERR_TOO_MANY_TOKENS;
+  if (ws == nullptr) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < layout(c, c->max_tokens).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return MOE_OK;
+}
+
+void record(void* const* ev, int idx, hipStream_t s) {
+  if (ev != nullptr && ev[idx] != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(ev[idx]), s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_TOO_MANY_TOKENS: return "more tokens than the configured maximum";
+    case MOE_ERR_UNSUPPORTED_FORMAT: return "unsupported expert format";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_check_arch(const char* arch) {
+  if (arch == nullptr) return MOE_ERR_INVALID_ARG;
+  if (std::strncmp(arch, "gfx950", 6) != 0) return MOE_ERR_UNSUPPORTED_DEVICE;
+  const char n = arch[6];
+  return (n == '\0' || n == ':') ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
+}
+
+int moe_validate_config(const moe_config* c) {
+  if (c == nullptr) return MOE_ERR_INVALID_ARG;
+  if (c->fmt != MOE_FMT_NVFP4 && c->fmt != MOE_FMT_MXFP8) return MOE_ERR_UNSUPPORTED_FORMAT;
+  if (c->hidden <= 0 || c->hidden % 128 != 0 || c->hidden > (1 << 16)) return MOE_ERR_INVALID_ARG;
+  if (c->ffn <= 0 || c->ffn % 128 != 0 || c->ffn > (1 << 16)) return MOE_ERR_INVALID_ARG;
+  if (c->num_experts < 1 || c->num_experts > 1024) return MOE_ERR_INVALID_ARG;
+  if (c->top_k < 1 || c->top_k > 32 || c->top_k > c->num_experts) return MOE_ERR_INVALID_ARG;
+  if (c->expert_begin < 0 || c->num_local_experts < 1 ||
+      c->expert_begin + c->num_local_experts > c->num_experts)
+    return MOE_ERR_INVALID_ARG;
+  if (c->cap_form < MOE_CAP_SOFT_GATE_UP || c->cap_form > MOE_CAP_NONE) return MOE_ERR_INVALID_ARG;
+  if (c->cap_form != MOE_CAP_NONE && !(c->cap > 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (c->max_tokens < 0 || (long)c->max_tokens * c->top_k > (1L << 26)) return MOE_ERR_INVALID_ARG;
+  // the GEMM work list rides grid.y (at most 65535 entries)
+  if (ceil_div((long)c->max_tokens * c->top_k, 32) + c->num_local_experts > 65535) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int moe_workspace_size(const moe_config* c, size_t* bytes) {
+  const int st = moe_validate_config(c);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  *bytes = layout(c, c->max_tokens).total;
+  return MOE_OK;
+}
+
+int moe_quantize_act(int32_t fmt, int32_t dtype, const void* x, int32_t rows, int32_t cols,
+                     uint8_t* codes, uint8_t* scales, float* row_gs, void* stream) {
+  if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8) return MOE_ERR_UNSUPPORTED_FORMAT;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
+  if (rows < 0 || cols <= 0 || cols % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID_ARG;
+  if (fmt == MOE_FMT_NVFP4 && row_gs == nullptr) return MOE_ERR_INVALID_ARG;
+  const int d = device_check();
+  if (d != MOE_OK) return d;
+  return launch_quant(fmt, dtype, x, rows, nullptr, cols, codes, scales, row_gs,
+                      static_cast<hipStream_t>(stream)) == 0 ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+int moe_route(const moe_config* c, const void* x, int32_t T, const void* w_router, const float* bias,
+              int32_t* topk_ids, float* topk_w, uint8_t* near_tie, void* ws, size_t ws_bytes,
+              void* stream) {
+  int st = moe_validate_config(c);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(c, T, ws, ws_bytes)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || w_router == nullptr || bias == nullptr || topk_ids == nullptr || topk_w == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if ((st = device_check()) != MOE_OK) return st;
+  const Layout L = layout(c, c->max_tokens);
+  return launch_router(static_cast<const uint16_t*>(x), T, c->hidden, static_cast<const uint16_t*>(w_router),
+                       bias, c->num_experts, c->top_k, c->norm_topk, c->routed_scale, at<float>(ws, L.z),
+                       topk_ids, topk_w, near_tie, static_cast<hipStream_t>(stream)) == 0
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+int moe_dispatch(const moe_config* c, const int32_t* topk_ids, int32_t T, int32_t* expert_offsets,
+                 int32_t* sorted_pairs, int32_t* pair_pos, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe_validate_config(c);
+  if (st != MOE_OK) return st;
+  if (T < 0 || expert_offsets == nullptr) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && topk_ids == nullptr) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(c, T, ws, ws_bytes)) != MOE_OK) return st;
+  if ((st = device_check()) != MOE_OK) return st;
+  const Layout L = layout(c, c->max_tokens);
+  DispatchBufs b;
+  b.counts = at<int32_t>(ws, L.counts);
+  b.offsets = expert_offsets;
+  b.sorted = sorted_pairs;
+  b.pos = pair_pos;
+  b.worklist = nullptr;
+  b.ntiles = nullptr;
+  return launch_dispatch(topk_ids, T * c->top_k, c->expert_begin, c->num_local_experts, 32, b,
+                         static_cast<hipStream_t>(stream)) == 0
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* topk_ids, const float* topk_w,
+                const moe_expert_weights* w, void* out, void* ws, size_t ws_bytes, void* stream,
+                void* const* events) {
+  int st = moe_validate_config(c);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(c, T, ws, ws_bytes)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || topk_ids == nullptr || topk_w == nullptr || w == nullptr || out == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (w->w13 == nullptr || w->w13_sc == nullptr || w->w2 == nullptr || w->w2_sc == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (c->fmt == MOE_FMT_NVFP4 && w->gs == nullptr) return MOE_ERR_INVALID_ARG;
+  if ((st = device_check()) != MOE_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout L = layout(c, c->max_tokens);
+  const int H = c->hidden, F = c->ffn, k = c->top_k, EL = c->num_local_experts;
+  const int P = T * k;
+  const bool nv = c->fmt == MOE_FMT_NVFP4;
+  int bad = 0;
+
+  // 1. quantize x per row
+  record(events, 2 * MOE_STAGE_QUANT_X, s);
+  bad |= launch_quant(c->fmt, 0, x, T, nullptr, H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs),
+                      at<float>(ws, L.xg), s);
+  record(events, 2 * MOE_STAGE_QUANT_X + 1, s);
+
+  // 2. dispatch + tile list
+  const int tile_m = gemm_tile_m(T, k, EL);
+  DispatchBufs b;
+  b.counts = at<int32_t>(ws, L.counts);
+  b.offsets = at<int32_t>(ws, L.offsets);
+  b.sorted = at<int32_t>(ws, L.sorted);
+  b.pos = at<int32_t>(ws, L.pos);
+  b.worklist = at<int32_t>(ws, L.work);
+  b.ntiles = at<int32_t>(ws, L.ntiles);
+  record(events, 2 * MOE_STAGE_DISPATCH, s);
+  bad |= launch_dispatch(topk_ids, P, c->expert_begin, EL, tile_m, b, s);
+  record(events, 2 * MOE_STAGE_DISPATCH + 1, s);
+
+  // 3. gate/up GEMM + capped SwiGLU -> h (fp32, sorted rows)
+  GemmArgs g;
+  g.fmt = c->fmt;
+  g.H = H;
+  g.F = F;
+  g.k = k;
+  g.E_local = EL;
+  g.a_codes = at<uint8_t>(ws, L.xq);
+  g.a_sc = at<uint8_t>(ws, L.xs);
+  g.a_gs = at<float>(ws, L.xg);
+  g.w_codes = w->w13;
+  g.w_sc = w->w13_sc;
+  g.w_gs = w->gs;
+  g.offsets = b.offsets;
+  g.sorted = b.sorted;
+  g.worklist = b.worklist;
+  g.ntiles = b.ntiles;
+  g.max_tiles = ceil_div((long)P, tile_m) + EL;
+  g.tile_m = tile_m;
+  g.cap_form = c->cap_form;
+  g.cap = c->cap_form == MOE_CAP_NONE ? 1.0f : c->cap;
+  g.out = at<float>(ws, L.h);
+  record(events, 2 * MOE_STAGE_GATE_UP, s);
+  bad |= launch_gemm_gateup(g, s);
+  record(events, 2 * MOE_STAGE_GATE_UP + 1, s);
+
+  // 4. quantize h per (token, expert) row; the row count lives on the device
+  record(events, 2 * MOE_STAGE_QUANT_H, s);
+  bad |= launch_quant(c->fmt, 1, at<float>(ws, L.h), P, b.offsets + EL, F, at<uint8_t>(ws, L.hq),
+                      at<uint8_t>(ws, L.hs), at<float>(ws, L.hg), s);
+  record(events, 2 * MOE_STAGE_QUANT_H + 1, s);
+
+  // 5. down GEMM -> y (fp32, sorted rows)
+  GemmArgs d = g;
+  d.a_codes = at<uint8_t>(ws, L.hq);
+  d.a_sc = at<uint8_t>(ws, L.hs);
+  d.a_gs = at<float>(ws, L.hg);
+  d.w_codes = w->w2;
+  d.w_sc = w->w2_sc;
+  d.out = at<float>(ws, L.y);
+  record(events, 2 * MOE_STAGE_DOWN, s);
+  bad |= launch_gemm_down(d, s);
+  record(events, 2 * MOE_STAGE_DOWN + 1, s);
+
+  // 6. combine
+  record(events, 2 * MOE_STAGE_COMBINE, s);
+  bad |= launch_combine(at<float>(ws, L.y), b.pos, topk_w, T, k, H, static_cast<uint16_t*>(out), s);
+  record(events, 2 * MOE_STAGE_COMBINE + 1, s);
+  (void)nv;
+  return bad ? MOE_ERR_LAUNCH : MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Deterministic weighted combine: out[t] = bf16_rne(sum_j w[t][j] * y[t, j])
+// summed in fixed j order over the pairs whose expert is local (the
+// "combine" stage of the SGLang cookbook's MegaMoE description, section 2).
+// y rows are in expert-sorted order; pair_pos maps pair t*k + j to its row
+// (-1: expert not local).  One workgroup per token, fp32 accumulation, no
+// atomics.  HBM-bound: reads k rows of fp32 y, writes one bf16 row.
+#include "moe_common.h"
+#include "launch.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const int32_t* __restrict__ pos,
+                                                 const float* __restrict__ w, int k, int H,
+                                                 uint16_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int32_t* pt = pos + (size_t)t * k;
+  const float* wt = w + (size_t)t * k;
+  for (int c = threadIdx.x; c < H / 4; c += 256) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; j++) {
+      const int p = pt[j];
+      if (p < 0) continue;
+      const float wj = wt[j];
+      const float4 v = reinterpret_cast<const float4*>(y + (size_t)p * H)[c];
+      acc.x += wj * v.x;
+      acc.y += wj * v.y;
+      acc.z += wj * v.z;
+      acc.w += wj * v.w;
+    }
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+    reinterpret_cast<uint2*>(out + (size_t)t * H)[c] = make_uint2(lo, hi);
+  }
+}
+
+int launch_combine(const float* y, const int32_t* pos, const float* w, int T, int k, int H,
+                   uint16_t* out, hipStream_t stream) {
+  if (T <= 0) return 0;
+  hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, stream, y, pos, w, k, H, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace moe

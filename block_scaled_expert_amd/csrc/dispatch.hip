@@ -1,0 +1,150 @@
+// Dispatch: a stable counting sort of the (token, slot) pair ids p = t*k + j
+// by local expert id, plus the per-expert tile work list the grouped GEMMs
+// walk.  This is the "dispatch" stage that precedes both expert GEMMs in the
+// SGLang cookbook's MegaMoE description (section 2, "MegaMoE").
+//
+// Four launches, no floating point and no order-deciding atomics:
+//   count   one workgroup per chunk of pairs: LDS histogram -> counts[c][e]
+//   scan    one workgroup per expert: exclusive scan of counts[*][e] over
+//           chunks (chunk order = pair order) -> per-chunk bases, totals[e]
+//   offsets one workgroup: exclusive scan of totals over experts; the GEMM
+//           tile list (local expert, first row) with tile_m rows per tile
+//   scatter one workgroup per chunk: each pair's rank among the earlier
+//           pairs of its expert inside the chunk, counted explicitly, gives
+//           its sorted position; integer atomics only accumulate counts.
+#include "moe_common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kSub = 256;   // pairs handled per pass of a 256-thread workgroup
+
+int dispatch_chunk(int P) {
+  // at most 1024 chunks so one 1024-thread workgroup can scan an expert
+  const int c = ceil_div(P, 1024);
+  return c <= kSub ? kSub : ceil_div(c, kSub) * kSub;
+}
+
+__global__ __launch_bounds__(256) void k_disp_count(const int32_t* __restrict__ ids, int P, int chunk,
+                                                    int E_begin, int E_local, int32_t* __restrict__ counts) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < E_local; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int c = blockIdx.x;
+  const int end = min(P, (c + 1) * chunk);
+  for (int p = c * chunk + threadIdx.x; p < end; p += 256) {
+    const int e = ids[p] - E_begin;
+    if (e >= 0 && e < E_local) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E_local; e += 256) counts[(size_t)c * E_local + e] = hist[e];
+}
+
+// grid = E_local, block = 1024; nchunks <= 1024.  counts[c][e] becomes the
+// number of pairs of expert e in chunks before c.
+__global__ __launch_bounds__(1024) void k_disp_scan(int32_t* __restrict__ counts, int nchunks, int E_local,
+                                                    int32_t* __restrict__ totals) {
+  __shared__ int32_t s[1024];
+  const int e = blockIdx.x, i = threadIdx.x;
+  const int v = i < nchunks ? counts[(size_t)i * E_local + e] : 0;
+  s[i] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {        // Hillis-Steele inclusive scan
+    const int add = i >= o ? s[i - o] : 0;
+    __syncthreads();
+    s[i] += add;
+    __syncthreads();
+  }
+  if (i < nchunks) counts[(size_t)i * E_local + e] = s[i] - v;
+  if (i == 1023) totals[e] = s[1023];
+}
+
+// One 1024-thread workgroup; E_local <= 1024.
+__global__ __launch_bounds__(1024) void k_disp_offsets(const int32_t* __restrict__ totals, int E_local,
+                                                       int tile_m, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ worklist,
+                                                       int32_t* __restrict__ ntiles) {
+  __shared__ int32_t s[1024], st[1024];
+  const int i = threadIdx.x;
+  const int n = i < E_local ? totals[i] : 0;
+  const int nt = (n + tile_m - 1) / tile_m;
+  s[i] = n;
+  st[i] = nt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int a = i >= o ? s[i - o] : 0;
+    const int b = i >= o ? st[i - o] : 0;
+    __syncthreads();
+    s[i] += a;
+    st[i] += b;
+    __syncthreads();
+  }
+  if (i < E_local) offsets[i] = s[i] - n;
+  if (i == 0) offsets[E_local] = s[1023];
+  if (i == 1023 && ntiles != nullptr) ntiles[0] = st[1023];
+  if (worklist != nullptr && i < E_local) {
+    const int base = st[i] - nt;
+    for (int j = 0; j < nt; j++) {
+      worklist[2 * (base + j)] = i;
+      worklist[2 * (base + j) + 1] = j * tile_m;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_disp_scatter(const int32_t* __restrict__ ids, int P, int chunk,
+                                                      int E_begin, int E_local,
+                                                      const int32_t* __restrict__ counts,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ sorted,
+                                                      int32_t* __restrict__ pos) {
+  extern __shared__ int32_t run[];            // [E_local] pairs already placed in this chunk
+  __shared__ int32_t sub[kSub];
+  for (int e = threadIdx.x; e < E_local; e += 256) run[e] = 0;
+  const int c = blockIdx.x;
+  const int begin = c * chunk, end = min(P, (c + 1) * chunk);
+  for (int p0 = begin; p0 < end; p0 += kSub) {
+    const int p = p0 + threadIdx.x;
+    int e = -1;
+    if (p < end) {
+      e = ids[p] - E_begin;
+      if (e < 0 || e >= E_local) e = -1;
+    }
+    __syncthreads();                           // previous pass done with sub / run
+    sub[threadIdx.x] = e;
+    __syncthreads();
+    int rank = 0;
+    for (int j = 0; j < kSub; j++) rank += (j < (int)threadIdx.x && sub[j] == e) ? 1 : 0;
+    if (p < end) {
+      if (e >= 0) {
+        const int q = offsets[e] + counts[(size_t)c * E_local + e] + run[e] + rank;
+        if (sorted != nullptr) sorted[q] = p;
+        if (pos != nullptr) pos[p] = q;
+      } else if (pos != nullptr) {
+        pos[p] = -1;
+      }
+    }
+    __syncthreads();                           // all ranks read run[] before it moves
+    if (e >= 0) atomicAdd(&run[e], 1);
+  }
+}
+
+int launch_dispatch(const int32_t* ids, int P, int E_begin, int E_local, int tile_m,
+                    const DispatchBufs& b, hipStream_t stream) {
+  const int chunk = dispatch_chunk(P > 0 ? P : 1);
+  const int nchunks = P > 0 ? ceil_div(P, chunk) : 0;
+  const size_t lds = (size_t)E_local * sizeof(int32_t);
+  int32_t* totals = b.counts + (size_t)(nchunks > 0 ? nchunks : 1) * E_local;
+  if (nchunks > 0)
+    hipLaunchKernelGGL(k_disp_count, dim3(nchunks), dim3(256), lds, stream, ids, P, chunk, E_begin,
+                       E_local, b.counts);
+  hipLaunchKernelGGL(k_disp_scan, dim3(E_local), dim3(1024), 0, stream, b.counts, nchunks, E_local,
+                     totals);
+  hipLaunchKernelGGL(k_disp_offsets, dim3(1), dim3(1024), 0, stream, totals, E_local, tile_m,
+                     b.offsets, b.worklist, b.ntiles);
+  if (nchunks > 0)
+    hipLaunchKernelGGL(k_disp_scatter, dim3(nchunks), dim3(256), lds, stream, ids, P, chunk, E_begin,
+                       E_local, b.counts, b.offsets, b.sorted, b.pos);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace moe

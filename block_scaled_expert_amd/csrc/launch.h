@@ -1,0 +1,68 @@
+// Internal launch wrappers of the MoE kernels (host side).  Argument
+// checking happens in api.hip before any of these is called; each wrapper
+// only enqueues work and returns 0, or -1 when hipGetLastError reports a
+// failed launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Activation quantization of `rows` rows (further limited by *rows_dev when
+// non-null) of width `cols`.  fmt: 1 NVFP4, 2 MXFP8.  dtype: 0 bf16, 1 fp32.
+int launch_quant(int fmt, int dtype, const void* x, int rows, const int* rows_dev, int cols,
+                 uint8_t* codes, uint8_t* scales, float* gs, hipStream_t stream);
+
+// Router: logits into z [T][E] (fp32 workspace), then sigmoid + bias + top-k.
+int launch_router(const uint16_t* x, int T, int H, const uint16_t* wr, const float* bias, int E,
+                  int k, int norm_topk, float routed_scale, float* z, int32_t* ids, float* w,
+                  uint8_t* near_tie, hipStream_t stream);
+
+// Dispatch workspace layout (all int32):
+//   counts [nchunks][E_local], totals [E_local], tiles: worklist [max_tiles] int2,
+//   ntiles [1].
+struct DispatchBufs {
+  int32_t* counts;      // [nchunks * E_local]
+  int32_t* offsets;     // [E_local + 1]
+  int32_t* sorted;      // [P] (nullable)
+  int32_t* pos;         // [P] (nullable)
+  int32_t* worklist;    // [2 * max_tiles] (nullable): (local expert, first row)
+  int32_t* ntiles;      // [1] (nullable)
+};
+int dispatch_chunk(int P);
+int launch_dispatch(const int32_t* ids, int P, int E_begin, int E_local, int tile_m,
+                    const DispatchBufs& b, hipStream_t stream);
+
+struct GemmArgs {
+  int fmt;                 // 1 NVFP4, 2 MXFP8
+  int H, F, k;
+  int E_local;
+  // activations (quantized rows)
+  const uint8_t* a_codes;  // gate/up: x codes [T][...]; down: h codes [P][...]
+  const uint8_t* a_sc;
+  const float* a_gs;       // NVFP4 row scales (nullable for MXFP8)
+  // weights
+  const uint8_t* w_codes;
+  const uint8_t* w_sc;
+  const float* w_gs;       // [E_local][3] (NVFP4)
+  // routing
+  const int32_t* offsets;  // [E_local+1]
+  const int32_t* sorted;   // [P] pair ids in expert order
+  const int32_t* worklist; // [2*max_tiles]
+  const int32_t* ntiles;   // [1]
+  int max_tiles;           // grid.y: an upper bound of *ntiles
+  int tile_m;              // rows per work-list entry (32 or 64; matches dispatch)
+  // epilogue
+  int cap_form;
+  float cap;
+  float* out;              // gate/up: h [P][F]; down: y [P][H] (rows in sorted order)
+};
+int gemm_tile_m(int T, int k, int E_local);
+int launch_gemm_gateup(const GemmArgs& a, hipStream_t stream);
+int launch_gemm_down(const GemmArgs& a, hipStream_t stream);
+
+int launch_combine(const float* y, const int32_t* pos, const float* w, int T, int k, int H,
+                   uint16_t* out, hipStream_t stream);
+
+}  // namespace moe

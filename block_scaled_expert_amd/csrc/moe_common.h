@@ -1,0 +1,124 @@
+// Internal helpers shared by the gfx950 kernels of the MoE library.
+//
+// Element formats (OCP MX / NVFP4 conventions that the pages' "NVFP4" and
+// "MXFP8" name; SGLang cookbook "Inkling-2-Small", section 2 "Checkpoints"):
+//   E2M1: sign, 2-bit exponent (bias 1), 1-bit mantissa; max 6.
+//   E4M3: sign, 4-bit exponent (bias 7), 3-bit mantissa; max 448; the
+//         all-ones magnitude is NaN and is never produced.
+//   E8M0: 2^(c-127).
+// Conversions round to nearest, ties to the even code, saturate to the
+// largest finite magnitude and keep the sign of zero; a NaN encodes as +0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+namespace moe {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__host__ __device__ inline float bits_f(uint32_t b) {
+  float f;
+  memcpy(&f, &b, 4);
+  return f;
+}
+__host__ __device__ inline uint32_t f_bits(float f) {
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  return b;
+}
+// 2^e as fp32 for e in [-126, 127].
+__host__ __device__ inline float pow2f(int e) { return bits_f((uint32_t)(e + 127) << 23); }
+
+// fp32 -> E4M3 code.  For |x| < 448 the magnitude is rounded on the grid of
+// its binade (2^(e-3), e = max(floor(log2|x|), -6)); the integer quotient's
+// parity is the code's parity, so rint's ties-to-even is the code's.
+__host__ __device__ inline uint32_t e4m3_encode(float x) {
+  const uint32_t b = f_bits(x);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a == a)) return 0u;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  int e = (int)((b >> 23) & 0xFFu) - 127;
+  e = e < -6 ? -6 : e;
+  const float q = rintf(a * pow2f(3 - e));
+  return sign | (uint32_t)((e + 7) * 8 + (int)q - 8);
+}
+
+__host__ __device__ inline float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  const float mag = e == 0 ? (float)m * pow2f(-9) : (float)(8u + m) * pow2f((int)e - 10);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// fp32 -> E2M1 code (same construction on the E2M1 grid).
+__host__ __device__ inline uint32_t e2m1_encode(float x) {
+  const uint32_t b = f_bits(x);
+  const uint32_t sign = (b >> 28) & 0x8u;
+  const float a = fabsf(x);
+  if (!(a == a)) return 0u;
+  if (a >= 6.0f) return sign | 7u;
+  int e = (int)((b >> 23) & 0xFFu) - 127;
+  e = e < 0 ? 0 : e;
+  const float q = rintf(a * pow2f(1 - e));
+  return sign | (uint32_t)((e + 1) * 2 + (int)q - 2);
+}
+
+// E8M0 exponent E for an MX block of 32 with max magnitude amax (E4M3
+// elements, emax 8): E = clamp(floor(log2 amax) - 8, -127, 127); -127 for a
+// zero block.  Subnormal amax has floor(log2) <= -127, so it clamps too.
+__host__ __device__ inline int mx_exponent(float amax) {
+  const uint32_t ef = (f_bits(amax) >> 23) & 0xFFu;
+  if (ef == 0) return -127;
+  const int e = (int)ef - 127 - 8;
+  return e < -127 ? -127 : e;
+}
+
+__device__ inline float bf16_to_f32(uint16_t h) { return bits_f((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t b = f_bits(f);
+  const uint32_t r = b + 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(r >> 16);
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ inline float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// Cap + SwiGLU on fp32 gate/up values (cap forms of enum moe_cap_form).
+__device__ inline float cap_swiglu(float g, float u, int form, float c, float inv_c) {
+  if (form == 0) {            // soft cap on gate and up
+    g = c * tanhf(g * inv_c);
+    u = c * tanhf(u * inv_c);
+  } else if (form == 1) {     // hard cap
+    g = fminf(g, c);
+    u = fminf(fmaxf(u, -c), c);
+  }
+  float h = g / (1.0f + expf(-g)) * u;
+  if (form == 2) h = c * tanhf(h * inv_c);
+  return h;
+}
+
+inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace moe

@@ -1,0 +1,210 @@
+/*
+ * moe.h -- C ABI of the block-scaled routed-expert MoE layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer is the Inkling 2 Small routed-expert MoE: a sigmoid router with
+ * an additive per-expert selection bias picks the top 8 of 384 experts (no
+ * shared experts); each expert is a capped SwiGLU FFN (hidden 4608, expert
+ * FFN 2304) stored block-scaled, NVFP4 in layers 0-39 and MXFP8 in layers
+ * 40-47, with W4A4 / W8A8 activation quantization.  Sources: TokenSpeed blog
+ * "TML Inkling 2 Small at Day 0", table "What's new in Inkling 2 Small" (MoE
+ * and Checkpoint rows); Miles docs "inkling-2-small" section 1 (sigmoid
+ * routing, soft-capped SwiGLU), section 2 (hidden 4608, FFN 2304) and
+ * section 5.3 (W4A4 / W8A8); SGLang cookbook "Inkling-2-Small" section 2
+ * ("Checkpoints", "Parallelism", "MegaMoE"); SGLang blog "SGLang and Miles
+ * Add Day-0 Support for Inkling 2 Small", section "Performance" (router
+ * sigmoid + bias + top-k fused, quantization folded into the expert GEMMs).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns and
+ *    frees every buffer, including the workspace.  The library never
+ *    allocates, frees or synchronizes; all work is enqueued on `stream` (a
+ *    hipStream_t, NULL = the default stream) in order.
+ *  - Return value: MOE_OK (0) or a negative status (moe_status_string).
+ *    Argument errors are detected on the host before anything is enqueued.
+ *    Faults inside kernels surface at the caller's next synchronization.
+ *  - Only gfx950 devices are accepted (MOE_ERR_UNSUPPORTED_DEVICE otherwise),
+ *    as the pages' ROCm recipes accept gfx950 only (SGLang cookbook section
+ *    2, "AMD").
+ *  - Inputs are assumed finite.
+ *  - The library is stateless apart from a per-device architecture check
+ *    cached on first use; calls on different streams do not share state
+ *    except through the caller's buffers.
+ *
+ * Element formats (little-endian bytes, rows contiguous):
+ *  - bf16 activations: [rows][cols] uint16 bit patterns.
+ *  - E2M1 (FP4) codes: two per byte, element 2i in the low nibble.
+ *  - E4M3 (FP8, finite variant, max 448) and E8M0 (power of two 2^(c-127))
+ *    scale bytes.
+ *  - NVFP4 = E2M1 elements, one E4M3 scale per 16 consecutive elements of a
+ *    row, and one fp32 scale per scale domain (a row of activations; one per
+ *    (expert, matrix) for weights).
+ *  - MXFP8 = E4M3 elements, one E8M0 scale per 32 consecutive elements.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,        /* null pointer, bad shape or config value */
+  MOE_ERR_UNSUPPORTED_DEVICE = -2, /* the current device is not gfx950 */
+  MOE_ERR_WORKSPACE_TOO_SMALL = -3,
+  MOE_ERR_TOO_MANY_TOKENS = -4,    /* T > cfg->max_tokens */
+  MOE_ERR_UNSUPPORTED_FORMAT = -5,
+  MOE_ERR_LAUNCH = -6,             /* a kernel launch failed (hipGetLastError) */
+  MOE_ERR_HIP = -7                 /* another HIP runtime call failed */
+};
+
+enum moe_fmt { MOE_FMT_NVFP4 = 1, MOE_FMT_MXFP8 = 2 };
+
+/* Cap applied around the SwiGLU; c = cfg->cap.
+ * SOFT_GATE_UP: g' = c tanh(g/c), u' = c tanh(u/c), h = silu(g') u'
+ * HARD_GATE_UP: g' = min(g, c), u' = clamp(u, -c, c), h = silu(g') u'
+ * SOFT_OUT:     h = c tanh(silu(g) u / c)
+ * NONE:         h = silu(g) u
+ * The pages call the SwiGLU "capped" (SGLang cookbook section 2, TokenSpeed
+ * table) and "soft-capped" (Miles docs section 1) without a formula; the
+ * default is SOFT_GATE_UP. */
+enum moe_cap_form {
+  MOE_CAP_SOFT_GATE_UP = 0,
+  MOE_CAP_HARD_GATE_UP = 1,
+  MOE_CAP_SOFT_OUT = 2,
+  MOE_CAP_NONE = 3
+};
+
+/* Enqueue values for moe_dtype arguments. */
+enum moe_dtype { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
+
+/* Layer configuration (host struct, read during the call only). */
+typedef struct moe_config {
+  int32_t hidden;             /* H: 4608 for Inkling 2 Small; multiple of 128 */
+  int32_t ffn;                /* F: expert FFN width, 2304; multiple of 128 */
+  int32_t num_experts;        /* E: 384; 1..1024 */
+  int32_t top_k;              /* k: 8; 1..min(E, 32) */
+  int32_t expert_begin;       /* first expert held by this GPU */
+  int32_t num_local_experts;  /* experts [expert_begin, expert_begin + n) are
+                                 computed here; pairs routed elsewhere are
+                                 skipped (an expert-parallel share) */
+  int32_t fmt;                /* enum moe_fmt of the expert weights and of the
+                                 activation quantization (W4A4 / W8A8) */
+  int32_t cap_form;           /* enum moe_cap_form */
+  float cap;                  /* c, e.g. 7.0 */
+  int32_t norm_topk;          /* 1: gate weights divided by their sum over k */
+  float routed_scale;         /* gate weights multiplied by this (1.0) */
+  int32_t max_tokens;         /* largest T the workspace is sized for */
+} moe_config;
+
+/* Expert weights of the LOCAL experts, canonical layout, expert-major.
+ * For local expert i (global id expert_begin + i), with H = hidden, F = ffn:
+ *  NVFP4: w13    [i][2F][H/2]   E2M1 codes; rows 0..F-1 gate, F..2F-1 up
+ *         w13_sc [i][2F][H/16]  E4M3 block scales
+ *         w2     [i][H][F/2]    E2M1 codes of the down projection
+ *         w2_sc  [i][H][F/16]   E4M3 block scales
+ *         gs     [i][3]         fp32 scales of gate, up, down
+ *  MXFP8: w13    [i][2F][H]     E4M3 codes; w13_sc [i][2F][H/32] E8M0
+ *         w2     [i][H][F]      E4M3 codes; w2_sc  [i][H][F/32]  E8M0
+ *         gs     unused (may be NULL). */
+typedef struct moe_expert_weights {
+  const uint8_t* w13;
+  const uint8_t* w13_sc;
+  const uint8_t* w2;
+  const uint8_t* w2_sc;
+  const float* gs;
+} moe_expert_weights;
+
+/* Optional per-stage timing: events[2*s] is recorded before stage s and
+ * events[2*s+1] after it, on `stream`.  Entries are hipEvent_t handles
+ * created by the caller; NULL entries are skipped. */
+enum moe_stage {
+  MOE_STAGE_QUANT_X = 0, MOE_STAGE_DISPATCH = 1, MOE_STAGE_GATE_UP = 2,
+  MOE_STAGE_QUANT_H = 3, MOE_STAGE_DOWN = 4, MOE_STAGE_COMBINE = 5,
+  MOE_STAGE_COUNT = 6
+};
+
+/* ---------------------------------------------------------------------- */
+
+/* Status text (static storage).  Host only. */
+const char* moe_status_string(int status);
+
+/* MOE_OK if the device architecture name (hipDeviceProp_t.gcnArchName, e.g.
+ * "gfx950:sramecc+:xnack-") names gfx950, else MOE_ERR_UNSUPPORTED_DEVICE.
+ * Pure host function; `arch` is a host string. */
+int moe_check_arch(const char* arch);
+
+/* Validate a configuration (host).  MOE_OK or MOE_ERR_INVALID_ARG /
+ * MOE_ERR_UNSUPPORTED_FORMAT. */
+int moe_validate_config(const moe_config* cfg);
+
+/* Bytes of workspace moe_route, moe_dispatch and moe_forward need for up to
+ * cfg->max_tokens tokens.  Host only; *bytes is a host pointer. */
+int moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Per-row activation quantization (the W4A4 / W8A8 step; Miles docs section
+ * 5.3).  x: [rows][cols] bf16 (dtype MOE_DTYPE_BF16) or fp32.  cols must be
+ * a multiple of 32.
+ *  NVFP4: codes [rows][cols/2], scales [rows][cols/16] E4M3, row_gs [rows]
+ *         fp32.  Per row: A = max|v|; gs = A/2688 (1 if A == 0); per block
+ *         of 16: s = E4M3(a_b / (6 gs)), codes E2M1(v * (1 / (s gs))), all
+ *         in IEEE fp32, round to nearest even, saturating; a zero scale
+ *         zeroes its block.  The fp32 scale spans the row's full width
+ *         (SGLang cookbook section 2, "Parallelism").
+ *  MXFP8: codes [rows][cols], scales [rows][cols/32] E8M0, row_gs unused.
+ *         Per block of 32: X = 2^(floor(log2 amax) - 8) (2^-127 for a zero
+ *         block), codes E4M3(v / X) saturating.
+ * The result is bit-identical to the definition above. */
+int moe_quantize_act(int32_t fmt, int32_t dtype, const void* x, int32_t rows, int32_t cols,
+                     uint8_t* codes, uint8_t* scales, float* row_gs, void* stream);
+
+/* Router (SGLang blog "Performance": sigmoid, bias and top-k in one step;
+ * Miles docs section 1: sigmoid routing, top-8 of 384).
+ *  x [T][H] bf16; w_router [E][H] bf16; bias [E] fp32.
+ *  z = x w_router^T (fp32 accumulation); s = sigmoid(z); the k experts with
+ *  the largest s + bias are chosen, listed in descending order, ties to the
+ *  lower expert index; topk_w[t][j] = s[id] / sum_j s[id_j] (if norm_topk)
+ *  times routed_scale.
+ *  Outputs: topk_ids [T][k] int32, topk_w [T][k] fp32, near_tie [T] uint8
+ *  (1 when the k-th and (k+1)-th selection scores differ by less than 1e-6;
+ *  may be NULL).  ws: workspace of ws_bytes (moe_workspace_size). */
+int moe_route(const moe_config* cfg, const void* x, int32_t T, const void* w_router,
+              const float* bias, int32_t* topk_ids, float* topk_w, uint8_t* near_tie,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch of (token, slot) pairs to the local experts: a stable counting
+ * sort of the pair ids p = t*k + j by expert id (the "dispatch" stage of the
+ * SGLang cookbook's MegaMoE description, section 2).
+ *  topk_ids [T][k] int32 (ids outside [0, E) are an error only in the sense
+ *  that they are treated as non-local).
+ *  expert_offsets [num_local+1]: pairs of local expert i occupy
+ *  sorted_pairs[expert_offsets[i] .. expert_offsets[i+1]), in increasing p.
+ *  pair_pos [T*k]: position of pair p in sorted_pairs, or -1 if its expert
+ *  is not local.  Any output may be NULL except expert_offsets. */
+int moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T,
+                 int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* The expert half of the layer for T tokens already routed (topk_ids /
+ * topk_w from moe_route, or replayed from elsewhere: Miles docs section 5.3,
+ * rollout routing replay):
+ *   x quantized per row in cfg->fmt; for each pair (t, j) whose expert e is
+ *   local: [g | u] = x_q[t] W13[e]^T, h = capped SwiGLU(g, u) (fp32),
+ *   h quantized per (t, e) row in cfg->fmt, y = h_q W2[e]^T (fp32);
+ *   out[t] = bf16_rne(sum_j topk_w[t][j] y[t, j]) summed in j order over
+ *   the local pairs (a partial sum when only some experts are local).
+ *  x [T][H] bf16; out [T][H] bf16.  weights: local experts (host struct
+ *  pointing at device arrays).  events: optional stage timing (host array of
+ *  2*MOE_STAGE_COUNT hipEvent_t, or NULL). */
+int moe_forward(const moe_config* cfg, const void* x, int32_t T, const int32_t* topk_ids,
+                const float* topk_w, const moe_expert_weights* weights, void* out,
+                void* ws, size_t ws_bytes, void* stream, void* const* events);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

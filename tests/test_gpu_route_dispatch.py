@@ -1,0 +1,116 @@
+"""moe_route and moe_dispatch on the GPU vs the oracle.
+
+Routing: the chosen expert sets must be identical for every token that is
+not a near tie (8th/9th selection-score gap >= 1e-6 on either side); for
+near ties the GPU's set must still be a valid top-k under the oracle's
+scores within the tie band.  Gate weights within 1e-5 relative.
+Dispatch: offsets, sorted pair ids and pair positions bit-identical.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import layer as L
+
+from _util import inputs, lib_cfg, oracle_cfg
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_route(bse, w, T=None):
+    import torch
+    x, wr, b = inputs(w, T)
+    T = x.shape[0]
+    cfg = lib_cfg(bse, w, max_tokens=T)
+    ws = bse.workspace(cfg)
+    ids = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
+    nt = torch.empty(T, dtype=torch.uint8, device="cuda")
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    wrt = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).cuda()
+    bse.route(cfg, xt, wrt, torch.from_numpy(b).cuda(), ids, tw, nt, ws)
+    torch.cuda.synchronize()
+    return x, wr, b, ids.cpu().numpy(), tw.cpu().numpy(), nt.cpu().numpy().astype(bool)
+
+
+def _check_route(w, x, wr, b, ids, tw, nt):
+    r = L.route(oracle_cfg(w), x, wr, b)
+    tie = r["near_tie"] | nt
+    k = w.top_k
+    for t in range(x.shape[0]):
+        gset, oset = set(ids[t].tolist()), set(r["topk_ids"][t].tolist())
+        assert len(gset) == k
+        if not tie[t]:
+            assert gset == oset, f"token {t}"
+            # same order as the oracle (descending score)
+            assert list(ids[t]) == list(r["topk_ids"][t]), f"token {t}"
+        else:
+            kth = np.sort(r["sel"][t])[::-1][k - 1]
+            assert all(r["sel"][t][e] >= kth - 2e-6 for e in gset), f"token {t}"
+    ref_w = L.gate_weights(oracle_cfg(w), r["scores"], ids)
+    assert np.allclose(tw, ref_w, rtol=1e-5, atol=1e-7)
+    return int(tie.sum())
+
+
+@pytest.mark.parametrize("key,T", [("tiny", None), ("decode_nvfp4", None), ("decode_mxfp8", None),
+                                   ("decode_nvfp4", 1), ("decode_nvfp4", 37)])
+def test_route_matches_oracle(gpu_lib, key, T):
+    w = synth.WORKLOADS[key]
+    got = _run_route(gpu_lib, w, T)
+    ties = _check_route(w, *got)
+    assert ties <= max(2, got[0].shape[0] // 20)
+
+
+def test_route_prefill_sampled(gpu_lib):
+    """The 16384-token prefill chunk (Zipf bias): every token routed on the
+    GPU, a sample of 1024 tokens re-routed by the oracle."""
+    w = synth.WORKLOADS["prefill_nvfp4"]
+    x, wr, b, ids, tw, nt = _run_route(gpu_lib, w)
+    sample = np.random.default_rng(0).choice(x.shape[0], 1024, replace=False)
+    _check_route(w, x[sample], wr, b, ids[sample], tw[sample], nt[sample])
+    # load skew produced by the Zipf bias
+    counts = np.bincount(ids.ravel(), minlength=w.experts)
+    assert counts.max() / counts.mean() > 3
+
+
+def _dispatch(bse, cfg, ids_np):
+    import torch
+    T, k = ids_np.shape
+    ws = bse.workspace(cfg)
+    off = torch.full((cfg.num_local + 1,), -7, dtype=torch.int32, device="cuda")
+    sp = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    pos = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    bse.dispatch(cfg, torch.from_numpy(ids_np).cuda(), off, sp, pos, ws)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), sp.cpu().numpy(), pos.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,E,k,begin,nloc", [
+    (1, 16, 2, 0, None), (16, 16, 2, 0, None), (64, 384, 8, 0, None), (192, 384, 8, 0, None),
+    (4096, 384, 8, 0, 48), (4096, 384, 8, 336, 48), (16384, 384, 8, 0, None), (333, 40, 5, 7, 13),
+    (40000, 384, 8, 0, None)])
+def test_dispatch_bit_exact(gpu_lib, T, E, k, begin, nloc):
+    g = np.random.default_rng(T + E)
+    # skewed expert choice, distinct within a token
+    p = np.arange(1, E + 1, dtype=np.float64) ** -1.1
+    p /= p.sum()
+    ids = np.stack([g.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    w = synth.Workload("d", "d", T, 128, E, k, 128, "mxfp8", 0, expert_begin=begin, num_local=nloc)
+    cfg = lib_cfg(gpu_lib, w, max_tokens=T)
+    off, sp, pos = _dispatch(gpu_lib, cfg, ids)
+    ro, rs, rp = L.dispatch(oracle_cfg(w), ids)
+    assert np.array_equal(off, ro)
+    n = ro[-1]
+    assert np.array_equal(sp[:n], rs)
+    assert np.array_equal(pos, rp)
+
+
+def test_dispatch_empty(gpu_lib):
+    import torch
+    w = synth.Workload("d", "d", 4, 128, 16, 2, 128, "mxfp8", 0)
+    cfg = lib_cfg(gpu_lib, w, max_tokens=4)
+    ws = gpu_lib.workspace(cfg)
+    off = torch.full((17,), -7, dtype=torch.int32, device="cuda")
+    gpu_lib.dispatch(cfg, torch.zeros((0, 2), dtype=torch.int32, device="cuda"), off, None, None, ws)
+    torch.cuda.synchronize()
+    assert off.cpu().numpy().tolist() == [0] * 17
