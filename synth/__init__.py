@@ -102,28 +102,34 @@ def expert_float_weights(seed: int, e: int, H: int, Fd: int, sigma: float = 0.02
     return gate, up, down
 
 
-# Direct-code weights: random valid encodings drawn straight from fixed
-# distributions (no quantizer involved), sized so that an element's RMS is
-# about 0.02 like the float recipe.  Used where encoding hundreds of
-# full-size experts from floats would take minutes.
-#   NVFP4: every nibble uniform over the 16 E2M1 codes; block-scale bytes
-#          uniform over E4M3 codes 0x68..0x7E (64 .. 448); fp32 scale per
-#          matrix 2^-15 * U(0.9, 1.1).
-#   MXFP8: E4M3 bytes with a random sign, exponent field uniform in 10..15 and
-#          a uniform mantissa (0x7F/0xFF remapped to 0x7E/0xFE); E8M0 scale
-#          bytes uniform in 112..114 (2^-15 .. 2^-13).
-NV_SCALE_LO, NV_SCALE_HI = 0x68, 0x7E
-MX_EXP_LO, MX_EXP_HI = 10, 15
-MX_SCALE_LO, MX_SCALE_HI = 112, 114
+# Direct-code weights: random valid encodings drawn straight from random
+# bytes (no quantizer involved), sized so that an element's RMS is about
+# 0.02 like the float recipe.  Used where encoding hundreds of full-size
+# experts from floats would take minutes.  With b a uniform random byte:
+#   NVFP4: code bytes = b (every nibble uniform over the 16 E2M1 codes);
+#          block-scale bytes 0x68 + (b & 0xF) (E4M3 64 .. 240); fp32 scale
+#          per matrix 2^-14 * U(0.9, 1.1).
+#   MXFP8: E4M3 bytes (b & 0x80) | min(0x50 | (b & 0x2F), 0x7E): random sign,
+#          exponent field in {10, 11, 14, 15}, any mantissa, never NaN;
+#          E8M0 scale bytes 112 + bit0(b) + bit1(b) (2^-15 .. 2^-13).
+
+
+def _bytes(g: np.random.Generator, shape) -> np.ndarray:
+    return np.frombuffer(g.bytes(int(np.prod(shape))), dtype=np.uint8).reshape(shape)
 
 
 def _mx_bytes(g: np.random.Generator, shape) -> np.ndarray:
-    sign = g.integers(0, 2, size=shape, dtype=np.uint8) << 7
-    ex = g.integers(MX_EXP_LO, MX_EXP_HI + 1, size=shape, dtype=np.uint8) << 3
-    man = g.integers(0, 8, size=shape, dtype=np.uint8)
-    b = sign | ex | man
-    b[(b & 0x7F) == 0x7F] -= 1
-    return b
+    b = _bytes(g, shape)
+    return (b & np.uint8(0x80)) | np.minimum(np.uint8(0x50) | (b & np.uint8(0x2F)), np.uint8(0x7E))
+
+
+def _mx_scales(g: np.random.Generator, shape, shift: int) -> np.ndarray:
+    b = _bytes(g, shape)
+    return (np.uint8(112 + shift) + (b & np.uint8(1)) + ((b >> np.uint8(1)) & np.uint8(1))).astype(np.uint8)
+
+
+def _nv_scales(g: np.random.Generator, shape) -> np.ndarray:
+    return np.uint8(0x68) + (_bytes(g, shape) & np.uint8(0xF))
 
 
 def expert_direct_codes(seed: int, e: int, H: int, Fd: int, fmt: str, gain: float = 1.0) -> dict:
@@ -132,18 +138,15 @@ def expert_direct_codes(seed: int, e: int, H: int, Fd: int, fmt: str, gain: floa
     round(log2 gain) (MXFP8); it is used to push activations into the cap."""
     g = rng(seed, 4, e)
     if fmt == "nvfp4":
-        w13 = g.integers(0, 256, size=(2 * Fd, H // 2), dtype=np.uint8)
-        w13_sc = g.integers(NV_SCALE_LO, NV_SCALE_HI + 1, size=(2 * Fd, H // 16), dtype=np.uint8)
-        w2 = g.integers(0, 256, size=(H, Fd // 2), dtype=np.uint8)
-        w2_sc = g.integers(NV_SCALE_LO, NV_SCALE_HI + 1, size=(H, Fd // 16), dtype=np.uint8)
-        gs = (np.float32(2.0 ** -15) * g.uniform(0.9, 1.1, size=3).astype(np.float32) * np.float32(gain))
+        w13 = _bytes(g, (2 * Fd, H // 2)).copy()
+        w13_sc = _nv_scales(g, (2 * Fd, H // 16))
+        w2 = _bytes(g, (H, Fd // 2)).copy()
+        w2_sc = _nv_scales(g, (H, Fd // 16))
+        gs = np.float32(2.0 ** -14) * g.uniform(0.9, 1.1, size=3).astype(np.float32) * np.float32(gain)
         return dict(w13=w13, w13_sc=w13_sc, w2=w2, w2_sc=w2_sc, gs=gs.astype(np.float32))
     if fmt == "mxfp8":
         sh = int(round(np.log2(gain)))
-        w13 = _mx_bytes(g, (2 * Fd, H))
-        w13_sc = (g.integers(MX_SCALE_LO, MX_SCALE_HI + 1, size=(2 * Fd, H // 32)) + sh).astype(np.uint8)
-        w2 = _mx_bytes(g, (H, Fd))
-        w2_sc = (g.integers(MX_SCALE_LO, MX_SCALE_HI + 1, size=(H, Fd // 32)) + sh).astype(np.uint8)
-        return dict(w13=w13, w13_sc=w13_sc, w2=w2, w2_sc=w2_sc)
+        return dict(w13=_mx_bytes(g, (2 * Fd, H)), w13_sc=_mx_scales(g, (2 * Fd, H // 32), sh),
+                    w2=_mx_bytes(g, (H, Fd)), w2_sc=_mx_scales(g, (H, Fd // 32), sh))
     raise ValueError(fmt)
 
