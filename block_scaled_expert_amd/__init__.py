@@ -16,7 +16,7 @@ import os
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmoe.so")
+LIB_PATH = os.environ.get("BSE_MOE_LIB") or os.path.join(HERE, "libmoe.so")
 
 FMT_NVFP4, FMT_MXFP8 = 1, 2
 FMTS = {"nvfp4": FMT_NVFP4, "mxfp8": FMT_MXFP8}

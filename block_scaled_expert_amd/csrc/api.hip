@@ -43,7 +43,7 @@ Layout layout(const moe_config* c, int T) {
   const size_t P = (size_t)T * k;
   const bool nv = c->fmt == MOE_FMT_NVFP4;
   L.nchunks = P > 0 ? ceil_div((long)P, dispatch_chunk((int)P)) : 0;
-  L.max_tiles = ceil_div((long)P, 32) + (int)EL;
+  L.max_tiles = ceil_div((long)P, 16) + (int)EL;   // smallest tile_m is 16
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -126,7 +126,7 @@ int moe_validate_config(const moe_config* c) {
   if (c->cap_form != MOE_CAP_NONE && !(c->cap > 0.0f)) return MOE_ERR_INVALID_ARG;
   if (c->max_tokens < 0 || (long)c->max_tokens * c->top_k > (1L << 26)) return MOE_ERR_INVALID_ARG;
   // the GEMM work list rides grid.y (at most 65535 entries)
-  if (ceil_div((long)c->max_tokens * c->top_k, 32) + c->num_local_experts > 65535) return MOE_ERR_INVALID_ARG;
+  if (ceil_div((long)c->max_tokens * c->top_k, 16) + c->num_local_experts > 65535) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 

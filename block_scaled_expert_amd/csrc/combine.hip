@@ -2,8 +2,8 @@
 // summed in fixed j order over the pairs whose expert is local (the
 // "combine" stage of the SGLang cookbook's MegaMoE description, section 2).
 // y rows are in expert-sorted order; pair_pos maps pair t*k + j to its row
-// (-1: expert not local).  One workgroup per token, fp32 accumulation, no
-// atomics.  HBM-bound: reads k rows of fp32 y, writes one bf16 row.
+// (-1: expert not local).  One workgroup per (token, 1024 columns), fp32
+// accumulation, no atomics.  HBM-bound: reads k rows of fp32 y, writes one bf16 row.
 #include "moe_common.h"
 #include "launch.h"
 
@@ -15,7 +15,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
   const int t = blockIdx.x;
   const int32_t* pt = pos + (size_t)t * k;
   const float* wt = w + (size_t)t * k;
-  for (int c = threadIdx.x; c < H / 4; c += 256) {
+  const int c = blockIdx.y * 256 + threadIdx.x;     // float4 column
+  if (c < H / 4) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; j++) {
       const int p = pt[j];
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
 int launch_combine(const float* y, const int32_t* pos, const float* w, int T, int k, int H,
                    uint16_t* out, hipStream_t stream) {
   if (T <= 0) return 0;
-  hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, stream, y, pos, w, k, H, out);
+  hipLaunchKernelGGL(k_combine, dim3(T, ceil_div(H / 4, 256)), dim3(256), 0, stream, y, pos, w, k, H, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -34,18 +34,26 @@
 
 namespace moe {
 
-// E2M1 x 8 (one 32-bit word, low nibble first) -> f16 x 8 scaled by sig.
+// E2M1 x 8 (one 32-bit word, low nibble first) -> f16 x 8, each times its
+// block scale.  The convert applies the power of two 2^8 (its scale operand
+// only contributes an exponent); the block scale enters as sigma * 2^-8 in
+// f16 (see sig_pair), so every product is exactly E2M1 * sigma: at most 7
+// significant bits, magnitudes 2^-10 .. 2688, all normal f16 numbers.
 __device__ inline v8h dequant8(uint32_t word, v2h sig2) {
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * sig2;
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * sig2;
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * sig2;
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * sig2;
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 0) * sig2;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 1) * sig2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 2) * sig2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 3) * sig2;
   return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-__device__ inline v2h e4m3_to_h2(uint32_t c) {
-  const _Float16 s = (_Float16)e4m3_decode(c);
-  return v2h{s, s};
+// Two E4M3 scale bytes (low 16 bits of w) -> f16 pair {sigma0, sigma1} * 2^-8.
+// Moving the E4M3 exponent/mantissa field 7 bits up lands it in the f16
+// exponent/mantissa field with the bias difference 8 = 15 - 7, so the f16
+// bit pattern is the E4M3 value times 2^-8, subnormals included.
+__device__ inline v2h sig_pair(uint32_t w) {
+  const uint32_t b = ((w & 0x7Fu) << 7) | ((w & 0x80u) << 8) | ((w & 0x7F00u) << 15) | ((w & 0x8000u) << 16);
+  return __builtin_bit_cast(v2h, b);
 }
 
 // One k step (128 elements) of operand data for one 16-row group.
@@ -86,30 +94,66 @@ __device__ inline v4f mma(const Frag8& a, const Frag8& b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, (int)a.sc, 0, (int)b.sc);
 }
 
-// NVFP4: expand both fragments and issue four f16 MFMAs.
+// NVFP4: expand a fragment into four f16 MFMA operands.
 struct Half4 {
   v8h v[4];
 };
 __device__ inline void expand(const Frag4& f, Half4& h) {
-  const v2h s0 = e4m3_to_h2(f.sc & 0xFF), s1 = e4m3_to_h2(f.sc >> 8);
+  const v2h sp = sig_pair(f.sc);
+  const v2h s0 = v2h{sp[0], sp[0]}, s1 = v2h{sp[1], sp[1]};
   h.v[0] = dequant8(f.q.x, s0);
   h.v[1] = dequant8(f.q.y, s0);
   h.v[2] = dequant8(f.q.z, s1);
   h.v[3] = dequant8(f.q.w, s1);
 }
-__device__ inline v4f mma(const Half4& a, const Half4& b, v4f c) {
+// One of the four 8-element MFMA operands of a fragment.
+__device__ inline v8h expand_part(const Frag4& f, int j) {
+  const v2h sp = sig_pair(f.sc);
+  const v2h sg = j < 2 ? v2h{sp[0], sp[0]} : v2h{sp[1], sp[1]};
+  const uint32_t w = j == 0 ? f.q.x : j == 1 ? f.q.y : j == 2 ? f.q.z : f.q.w;
+  return dequant8(w, sg);
+}
+
+// Work of one k step for one wave: MS row subtiles x NCG column groups.
+// The MFMAs are ordered so consecutive ones update different accumulators.
+template <int FMT, int MS, int NCG, typename Frag>
+__device__ inline void step_compute(const Frag* fa, const Frag* fb, v4f (*acc)[NCG]) {
+  if constexpr (FMT == 2) {
 #pragma unroll
-  for (int j = 0; j < 4; j++) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.v[j], b.v[j], c, 0, 0, 0);
-  return c;
+    for (int i = 0; i < MS; i++)
+#pragma unroll
+      for (int c = 0; c < NCG; c++) acc[i][c] = mma(fa[i], fb[c], acc[i][c]);
+  } else {
+    Half4 ha[MS];
+#pragma unroll
+    for (int i = 0; i < MS; i++) expand(fa[i], ha[i]);
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int c = 0; c < NCG; c++) {
+        const v8h hb = expand_part(fb[c], j);
+#pragma unroll
+        for (int i = 0; i < MS; i++)
+          acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ha[i].v[j], hb, acc[i][c], 0, 0, 0);
+      }
+  }
 }
 
 // STAGE 0: gate/up (A = x codes gathered by token, B = w13, out = h [P][F]).
+//   Workgroup tile: 64 rows of w13 (32 gate rows and the matching 32 up rows).
+//   The 4 waves split K four ways (KS = 4, NS = 1).
 // STAGE 1: down (A = h codes in sorted order, B = w2, out = y [P][H]).
-template <int FMT, int STAGE, int MS>
+//   Workgroup tile: 64 rows of w2.  Waves split K two ways and the 64 rows
+//   two ways (KS = 2, NS = 2).
+// NST > 0: every wave runs exactly NST k steps (K = 128 * NST * KS), fully
+// unrolled with no branch in the step sequence; NST == 0: any K, runtime
+// trip counts.
+template <int FMT, int STAGE, int MS, int PF, int NST>
 __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
-  constexpr int TM = 16 * MS, BN = 64, NCG = 4;
+  constexpr int KS = STAGE == 0 ? 4 : 2, NS = 4 / KS;
+  constexpr int TM = 16 * MS, BN = 64, NCG = 4 / NS;
   typedef typename std::conditional<FMT == 2, Frag8, Frag4>::type Frag;
-  __shared__ float red[4][TM][BN + 1];
+  __shared__ float red[KS][TM][BN + 1];
   __shared__ int tok[TM];
 
   const int tile = blockIdx.y;
@@ -119,6 +163,7 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
   const int rows = min(TM, a.offsets[el + 1] - row0);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kpart = wave % KS, npart = wave / KS;
   const int r = lane & 15, g = lane >> 4;
   const int K = STAGE == 0 ? a.H : a.F;
   const int NW = STAGE == 0 ? 2 * a.F : a.H;              // rows of the weight matrix
@@ -127,35 +172,37 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
   const uint8_t* wexp = a.w_codes + (size_t)el * NW * row_bytes;
   const uint8_t* wsexp = a.w_sc + (size_t)el * NW * sc_bytes;
 
+  // weight rows of this lane (column groups of 16 output columns)
+  const uint8_t* brow[NCG];
+  const uint8_t* bsrow[NCG];
+#pragma unroll
+  for (int c = 0; c < NCG; c++) {
+    const int cg = npart * NCG + c;   // 0..3 within the 64-row tile
+    int n;
+    if (STAGE == 0)   // column groups 0,1: gate rows; 2,3: the matching up rows
+      n = (cg < 2 ? 0 : a.F) + blockIdx.x * 32 + 16 * (cg & 1) + r;
+    else
+      n = blockIdx.x * BN + 16 * cg + r;
+    brow[c] = wexp + (size_t)n * row_bytes;
+    bsrow[c] = wsexp + (size_t)n * sc_bytes;
+  }
+
   if (threadIdx.x < TM) {
     const int m = threadIdx.x;
     tok[m] = m < rows ? (STAGE == 0 ? a.sorted[row0 + m] / a.k : row0 + m) : -1;
   }
   __syncthreads();
 
-  // rows of this lane's operands
+  // activation rows of this lane; rows past the tile read the tile's first
+  // row (MFMA rows are independent, their outputs are discarded)
   const uint8_t* arow[MS];
   const uint8_t* asrow[MS];
-  bool avalid[MS];
 #pragma unroll
   for (int i = 0; i < MS; i++) {
     const int t = tok[16 * i + r];
-    avalid[i] = t >= 0;
-    const int tt = t >= 0 ? t : 0;
+    const int tt = t >= 0 ? t : tok[0];
     arow[i] = a.a_codes + (size_t)tt * row_bytes;
     asrow[i] = a.a_sc + (size_t)tt * sc_bytes;
-  }
-  const uint8_t* brow[NCG];
-  const uint8_t* bsrow[NCG];
-#pragma unroll
-  for (int c = 0; c < NCG; c++) {
-    int n;
-    if (STAGE == 0)   // column groups 0,1: gate rows; 2,3: the matching up rows
-      n = (c < 2 ? 0 : a.F) + blockIdx.x * 32 + 16 * (c & 1) + r;
-    else
-      n = blockIdx.x * BN + 16 * c + r;
-    brow[c] = wexp + (size_t)n * row_bytes;
-    bsrow[c] = wsexp + (size_t)n * sc_bytes;
   }
 
   v4f acc[MS][NCG];
@@ -164,52 +211,40 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
 #pragma unroll
     for (int c = 0; c < NCG; c++) acc[i][c] = v4f{0, 0, 0, 0};
 
-  const int nsteps = K / 128;
-  const int s0 = wave * nsteps / 4, s1 = (wave + 1) * nsteps / 4;
-  Frag fa[MS], fb[NCG];
-  if (s0 < s1) {
+  // Ring of PF k steps in flight.  No load sits under a branch: a divergent
+  // or conditional load makes the compiler drain every outstanding load at
+  // the join, which serializes the pipeline.
+  Frag fa[PF][MS], fb[PF][NCG];
+  auto issue = [&](int step, Frag* A, Frag* B) {
 #pragma unroll
-    for (int c = 0; c < NCG; c++) load_frag(fb[c], brow[c], bsrow[c], s0 * 128, g);
+    for (int c = 0; c < NCG; c++) load_frag(B[c], brow[c], bsrow[c], step * 128, g);
 #pragma unroll
-    for (int i = 0; i < MS; i++) {
-      if (avalid[i]) load_frag(fa[i], arow[i], asrow[i], s0 * 128, g);
-      else zero_frag(fa[i]);
+    for (int i = 0; i < MS; i++) load_frag(A[i], arow[i], asrow[i], step * 128, g);
+  };
+  if constexpr (NST > 0) {
+    const int s0 = kpart * NST;
+#pragma unroll
+    for (int j = 0; j < PF && j < NST; j++) issue(s0 + j, fa[j], fb[j]);
+#pragma unroll
+    for (int s = 0; s < NST; s++) {
+      step_compute<FMT, MS, NCG>(fa[s % PF], fb[s % PF], acc);
+      if (s + PF < NST) issue(s0 + s + PF, fa[s % PF], fb[s % PF]);
     }
-  }
-  for (int s = s0; s < s1; s++) {
-    Frag na[MS], nb[NCG];
-    const bool more = s + 1 < s1;
-    if (more) {
+  } else {
+    const int nsteps = K / 128;
+    const int s0 = kpart * nsteps / KS, s1 = (kpart + 1) * nsteps / KS;
+    const int slast = s1 - 1;
+    if (s0 < s1) {
 #pragma unroll
-      for (int c = 0; c < NCG; c++) load_frag(nb[c], brow[c], bsrow[c], (s + 1) * 128, g);
+      for (int j = 0; j < PF; j++) issue(min(s0 + j, slast), fa[j], fb[j]);
+    }
+    // steps past the wave's range re-read its last step (a cache hit)
+    for (int s = s0; s < s1; s += PF) {
 #pragma unroll
-      for (int i = 0; i < MS; i++) {
-        if (avalid[i]) load_frag(na[i], arow[i], asrow[i], (s + 1) * 128, g);
-        else zero_frag(na[i]);
+      for (int j = 0; j < PF; j++) {
+        if (s + j < s1) step_compute<FMT, MS, NCG>(fa[j], fb[j], acc);
+        issue(min(s + j + PF, slast), fa[j], fb[j]);
       }
-    }
-    if constexpr (FMT == 2) {
-#pragma unroll
-      for (int i = 0; i < MS; i++)
-#pragma unroll
-        for (int c = 0; c < NCG; c++) acc[i][c] = mma(fa[i], fb[c], acc[i][c]);
-    } else {
-      Half4 hb[NCG];
-#pragma unroll
-      for (int c = 0; c < NCG; c++) expand(fb[c], hb[c]);
-#pragma unroll
-      for (int i = 0; i < MS; i++) {
-        Half4 ha;
-        expand(fa[i], ha);
-#pragma unroll
-        for (int c = 0; c < NCG; c++) acc[i][c] = mma(ha, hb[c], acc[i][c]);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int c = 0; c < NCG; c++) fb[c] = nb[c];
-#pragma unroll
-      for (int i = 0; i < MS; i++) fa[i] = na[i];
     }
   }
 
@@ -219,16 +254,21 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
 #pragma unroll
     for (int c = 0; c < NCG; c++)
 #pragma unroll
-      for (int q = 0; q < 4; q++) red[wave][16 * i + 4 * g + q][16 * c + r] = acc[i][c][q];
+      for (int q = 0; q < 4; q++) red[kpart][16 * i + 4 * g + q][16 * (npart * NCG + c) + r] = acc[i][c][q];
   __syncthreads();
 
+  auto ksum = [&](int m, int c) {
+    float v = red[0][m][c];
+#pragma unroll
+    for (int p = 1; p < KS; p++) v += red[p][m][c];
+    return v;
+  };
   if (STAGE == 0) {
     const float inv_c = 1.0f / a.cap;
     for (int idx = threadIdx.x; idx < TM * 32; idx += 256) {
       const int m = idx >> 5, c = idx & 31;
       if (m >= rows) continue;
-      float gv = ((red[0][m][c] + red[1][m][c]) + red[2][m][c]) + red[3][m][c];
-      float uv = ((red[0][m][32 + c] + red[1][m][32 + c]) + red[2][m][32 + c]) + red[3][m][32 + c];
+      float gv = ksum(m, c), uv = ksum(m, 32 + c);
       if (FMT == 1) {
         const float ga = a.a_gs[tok[m]];
         gv = (gv * ga) * a.w_gs[3 * el + 0];
@@ -241,7 +281,7 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
     for (int idx = threadIdx.x; idx < TM * BN; idx += 256) {
       const int m = idx >> 6, c = idx & 63;
       if (m >= rows) continue;
-      float yv = ((red[0][m][c] + red[1][m][c]) + red[2][m][c]) + red[3][m][c];
+      float yv = ksum(m, c);
       if (FMT == 1) yv = (yv * a.a_gs[row0 + m]) * a.w_gs[3 * el + 2];
       a.out[(size_t)(row0 + m) * a.H + blockIdx.x * BN + c] = yv;
     }
@@ -249,24 +289,37 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
 }
 
 int gemm_tile_m(int T, int k, int E_local) {
-  // average rows per local expert; small batches use 32-row tiles
-  const long pairs = (long)T * k;
-  return pairs / (E_local > 0 ? E_local : 1) > 24 ? 64 : 32;
+  // average rows per local expert decides the rows per work-list entry
+  const long avg = (long)T * k / (E_local > 0 ? E_local : 1);
+  return avg <= 2 ? 16 : (avg <= 24 ? 32 : 64);
 }
 
 static int launch_any(const GemmArgs& a, int stage, hipStream_t stream) {
   const dim3 block(256);
   const dim3 grid(stage == 0 ? a.F / 32 : a.H / 64, a.max_tiles);
-  const bool big = a.tile_m == 64;
-#define MOE_LAUNCH(FMT, ST, MS) \
-  hipLaunchKernelGGL((k_expert_gemm<FMT, ST, MS>), grid, block, 0, stream, a)
+  // Inkling 2 Small: H = 4608 gives 36 k steps = 4 waves x 9 (gate/up);
+  // F = 2304 gives 18 = 2 waves x 9 (down).
+  const bool fast = stage == 0 ? a.H == 128 * 9 * 4 : a.F == 128 * 9 * 2;
+#define MOE_LAUNCH(FMT, ST, MS, NST) \
+  hipLaunchKernelGGL((k_expert_gemm<FMT, ST, MS, (FMT == 1 ? 3 : 2), NST>), grid, block, 0, stream, a)
+#define MOE_LAUNCH_N(FMT, ST, MS)                  \
+  do {                                             \
+    if (fast) MOE_LAUNCH(FMT, ST, MS, 9);          \
+    else MOE_LAUNCH(FMT, ST, MS, 0);               \
+  } while (0)
+#define MOE_LAUNCH_MS(FMT, ST)                        \
+  do {                                                \
+    if (a.tile_m == 16) MOE_LAUNCH_N(FMT, ST, 1);     \
+    else if (a.tile_m == 32) MOE_LAUNCH_N(FMT, ST, 2); \
+    else MOE_LAUNCH_N(FMT, ST, 4);                    \
+  } while (0)
   if (a.fmt == 2) {
-    if (stage == 0) { if (big) MOE_LAUNCH(2, 0, 4); else MOE_LAUNCH(2, 0, 2); }
-    else            { if (big) MOE_LAUNCH(2, 1, 4); else MOE_LAUNCH(2, 1, 2); }
+    if (stage == 0) MOE_LAUNCH_MS(2, 0); else MOE_LAUNCH_MS(2, 1);
   } else {
-    if (stage == 0) { if (big) MOE_LAUNCH(1, 0, 4); else MOE_LAUNCH(1, 0, 2); }
-    else            { if (big) MOE_LAUNCH(1, 1, 4); else MOE_LAUNCH(1, 1, 2); }
+    if (stage == 0) MOE_LAUNCH_MS(1, 0); else MOE_LAUNCH_MS(1, 1);
   }
+#undef MOE_LAUNCH_MS
+#undef MOE_LAUNCH_N
 #undef MOE_LAUNCH
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -52,7 +52,7 @@ struct GemmArgs {
   const int32_t* worklist; // [2*max_tiles]
   const int32_t* ntiles;   // [1]
   int max_tiles;           // grid.y: an upper bound of *ntiles
-  int tile_m;              // rows per work-list entry (32 or 64; matches dispatch)
+  int tile_m;              // rows per work-list entry (16, 32 or 64; matches dispatch)
   // epilogue
   int cap_form;
   float cap;

@@ -2,7 +2,7 @@
 // section 5.3; the NVFP4 fp32 scale spans each row's full width: SGLang
 // cookbook "Inkling-2-Small" section 2, "Parallelism").
 //
-// One wavefront per row; lanes take whole scale blocks (16 elements for
+// One workgroup per row; threads take whole scale blocks (16 elements for
 // NVFP4, 32 for MXFP8), so loads are contiguous 32/64-byte runs across the
 // wave.  HBM-bound: every input byte is read once from HBM (the NVFP4 second
 // pass hits the cache) and every output byte written once.
@@ -46,15 +46,25 @@ __device__ inline void load_block<float>(const float* p, int n, float* v) {
   }
 }
 
-// NVFP4 rows.  rows_dev (nullable): device row count that further limits rows.
+// Row amax across the workgroup (256 threads = 4 waves).
+__device__ inline float block_max(float v, float* lds) {
+  v = wave_max(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds[wave] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(lds[0], lds[1]), fmaxf(lds[2], lds[3]));
+}
+
+// NVFP4 rows: one workgroup per row, one 16-element block per thread and
+// pass.  rows_dev (nullable): device row count that further limits rows.
 template <typename InT>
 __global__ __launch_bounds__(256) void k_quant_nvfp4(const InT* __restrict__ x, int rows,
                                                      const int* __restrict__ rows_dev, int cols,
                                                      uint8_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales,
                                                      float* __restrict__ gs_out) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ float red[4];
+  const int row = blockIdx.x;
   int nrows = rows;
   if (rows_dev != nullptr) nrows = min(nrows, *rows_dev);
   if (row >= nrows) return;
@@ -62,21 +72,21 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(const InT* __restrict__ x, 
   const int nblk = cols / 16;
 
   float A = 0.0f;
-  for (int b = lane; b < nblk; b += kWave) {
+  for (int b = threadIdx.x; b < nblk; b += 256) {
     float v[16];
     load_block<InT>(xr + 16 * b, 16, v);
 #pragma unroll
     for (int i = 0; i < 16; i++) A = fmaxf(A, fabsf(v[i]));
   }
-  A = wave_max(A);
+  A = block_max(A, red);
   const bool zero_row = (A == 0.0f);
   const float gs = zero_row ? 1.0f : __fdiv_rn(A, 2688.0f);
   const float denom = __fmul_rn(6.0f, gs);
-  if (lane == 0) gs_out[row] = gs;
+  if (threadIdx.x == 0) gs_out[row] = gs;
 
   uint8_t* cr = codes + (size_t)row * (cols / 2);
   uint8_t* sr = scales + (size_t)row * nblk;
-  for (int b = lane; b < nblk; b += kWave) {
+  for (int b = threadIdx.x; b < nblk; b += 256) {
     float v[16];
     load_block<InT>(xr + 16 * b, 16, v);
     float ab = 0.0f;
@@ -98,14 +108,13 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(const InT* __restrict__ x, 
   }
 }
 
-// MXFP8 rows.
+// MXFP8 rows: one workgroup per row, one 32-element block per thread and pass.
 template <typename InT>
 __global__ __launch_bounds__(256) void k_quant_mxfp8(const InT* __restrict__ x, int rows,
                                                      const int* __restrict__ rows_dev, int cols,
                                                      uint8_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x;
   int nrows = rows;
   if (rows_dev != nullptr) nrows = min(nrows, *rows_dev);
   if (row >= nrows) return;
@@ -113,7 +122,7 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(const InT* __restrict__ x, 
   const int nblk = cols / 32;
   uint8_t* cr = codes + (size_t)row * cols;
   uint8_t* sr = scales + (size_t)row * nblk;
-  for (int b = lane; b < nblk; b += kWave) {
+  for (int b = threadIdx.x; b < nblk; b += 256) {
     float v[32];
     load_block<InT>(xr + 32 * b, 32, v);
     float am = 0.0f;
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(256) void k_quant_mxfp8(const InT* __restrict__ x, 
 int launch_quant(int fmt, int dtype, const void* x, int rows, const int* rows_dev, int cols,
                  uint8_t* codes, uint8_t* scales, float* gs, hipStream_t stream) {
   if (rows <= 0) return 0;
-  const dim3 grid(ceil_div(rows, 4)), block(256);
+  const dim3 grid(rows), block(256);
   if (fmt == 1) {
     if (dtype == 0)
       hipLaunchKernelGGL(k_quant_nvfp4<uint16_t>, grid, block, 0, stream,
