@@ -114,6 +114,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--layout", choices=["packed", "canonical"], default="packed",
+                    help="expert weight layout (packed: moe_prepare_weights at load time)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -140,6 +142,11 @@ def main() -> int:
     t0 = time.time()
     wdev, per_expert = upload_weights(w, cfg)
     log(f"weights generated and uploaded in {time.time() - t0:.1f} s")
+    if args.layout == "packed":
+        canon = wdev
+        wdev = bse.prepare_weights(cfg, canon)
+        torch.cuda.synchronize()
+        del canon
     cw = bse.weights_struct(cfg, wdev)
     xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     wrt = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).cuda()
@@ -213,7 +220,8 @@ def main() -> int:
         "vs_baseline": None, "dtype": {"nvfp4": "nvfp4 (W4A4, fp32 acc)", "mxfp8": "mxfp8 (W8A8, fp32 acc)"}[w.fmt],
         "data": "synthetic (seeded; expert weights drawn as codes)",
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "ffn": w.ffn,
-                   "format": w.fmt, "local_experts": cfg.num_local, "parallelism": "single GPU"},
+                   "format": w.fmt, "local_experts": cfg.num_local, "weight_layout": args.layout,
+                   "parallelism": "single GPU"},
         "roofline": roof,
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "expert_weight_GBs": round(expert_bytes / (ms * 1e-3) / 1e9, 1),

@@ -25,7 +25,8 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 STAGES = ("quant_x", "dispatch", "gate_up", "quant_h", "down", "combine")
 
 EXPORTED = ("moe_status_string", "moe_check_arch", "moe_validate_config", "moe_workspace_size",
-            "moe_quantize_act", "moe_route", "moe_dispatch", "moe_forward")
+            "moe_quantize_act", "moe_route", "moe_dispatch", "moe_prepare_weights", "moe_forward")
+LAYOUT_CANONICAL, LAYOUT_PACKED = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -44,7 +45,7 @@ class CConfig(ctypes.Structure):
 
 class CWeights(ctypes.Structure):
     _fields_ = [("w13", ctypes.c_void_p), ("w13_sc", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("w2_sc", ctypes.c_void_p), ("gs", ctypes.c_void_p)]
+                ("w2_sc", ctypes.c_void_p), ("gs", ctypes.c_void_p), ("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -67,6 +68,8 @@ def load() -> ctypes.CDLL:
     lib.moe_quantize_act.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp]
     lib.moe_route.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_dispatch.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_prepare_weights.argtypes = [ctypes.POINTER(CConfig), ctypes.POINTER(CWeights), ctypes.POINTER(CWeights),
+                                        vp]
     lib.moe_forward.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, ctypes.POINTER(CWeights), vp, vp,
                                 sz, vp, vp]
     for name in EXPORTED:
@@ -190,7 +193,8 @@ def dispatch(cfg: Config, topk_ids, expert_offsets, sorted_pairs=None, pair_pos=
 
 
 def weights_struct(cfg: Config, w: dict) -> CWeights:
-    """w: dict of device tensors w13, w13_sc, w2, w2_sc (uint8) and gs (fp32, NVFP4)."""
+    """w: dict of device tensors w13, w13_sc, w2, w2_sc (uint8), gs (fp32,
+    NVFP4) and optionally layout (LAYOUT_CANONICAL by default)."""
     import torch
     H, F, n = cfg.hidden, cfg.ffn, cfg.num_local
     nv = cfg.fmt == "nvfp4"
@@ -200,7 +204,23 @@ def weights_struct(cfg: Config, w: dict) -> CWeights:
     }
     ptrs = {k: _ptr(w[k], torch.uint8, s, k) for k, s in shapes.items()}
     gs = _ptr(w["gs"], torch.float32, (n, 3), "gs") if nv else None
-    return CWeights(ptrs["w13"], ptrs["w13_sc"], ptrs["w2"], ptrs["w2_sc"], gs)
+    return CWeights(ptrs["w13"], ptrs["w13_sc"], ptrs["w2"], ptrs["w2_sc"], gs, int(w.get("layout", LAYOUT_CANONICAL)))
+
+
+def prepare_weights(cfg: Config, w: dict) -> dict:
+    """Repack canonical expert weights into the packed layout (new device
+    tensors of the same shapes; gs is shared)."""
+    import torch
+    src = weights_struct(cfg, w)
+    out = {k: torch.empty_like(w[k]) for k in ("w13", "w13_sc", "w2", "w2_sc")}
+    if "gs" in w:
+        out["gs"] = w["gs"]
+    out["layout"] = LAYOUT_PACKED
+    dst = weights_struct(cfg, out)
+    cc = cfg.c()
+    _ok(load().moe_prepare_weights(ctypes.byref(cc), ctypes.byref(src), ctypes.byref(dst), _stream()),
+        "moe_prepare_weights")
+    return out
 
 
 def forward(cfg: Config, x, topk_ids, topk_w, weights, out, ws, events=None) -> None:

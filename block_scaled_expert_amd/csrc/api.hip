@@ -193,6 +193,29 @@ int moe_dispatch(const moe_config* c, const int32_t* topk_ids, int32_t T, int32_
              : MOE_ERR_LAUNCH;
 }
 
+int moe_prepare_weights(const moe_config* c, const moe_expert_weights* src, moe_expert_weights* dst,
+                        void* stream) {
+  int st = moe_validate_config(c);
+  if (st != MOE_OK) return st;
+  if (src == nullptr || dst == nullptr) return MOE_ERR_INVALID_ARG;
+  if (src->layout != MOE_LAYOUT_CANONICAL) return MOE_ERR_INVALID_ARG;
+  if (src->w13 == nullptr || src->w13_sc == nullptr || src->w2 == nullptr || src->w2_sc == nullptr ||
+      dst->w13 == nullptr || dst->w13_sc == nullptr || dst->w2 == nullptr || dst->w2_sc == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (src->w13 == dst->w13 || src->w2 == dst->w2 || src->w13_sc == dst->w13_sc || src->w2_sc == dst->w2_sc)
+    return MOE_ERR_INVALID_ARG;
+  if ((st = device_check()) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long n = c->num_local_experts;
+  int bad = launch_pack(c->fmt, src->w13, src->w13_sc, n, 2 * c->ffn, c->hidden, const_cast<uint8_t*>(dst->w13),
+                        const_cast<uint8_t*>(dst->w13_sc), s);
+  bad |= launch_pack(c->fmt, src->w2, src->w2_sc, n, c->hidden, c->ffn, const_cast<uint8_t*>(dst->w2),
+                     const_cast<uint8_t*>(dst->w2_sc), s);
+  if (bad) return MOE_ERR_LAUNCH;
+  dst->layout = MOE_LAYOUT_PACKED;
+  return MOE_OK;
+}
+
 int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* topk_ids, const float* topk_w,
                 const moe_expert_weights* w, void* out, void* ws, size_t ws_bytes, void* stream,
                 void* const* events) {
@@ -206,6 +229,7 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   if (w->w13 == nullptr || w->w13_sc == nullptr || w->w2 == nullptr || w->w2_sc == nullptr)
     return MOE_ERR_INVALID_ARG;
   if (c->fmt == MOE_FMT_NVFP4 && w->gs == nullptr) return MOE_ERR_INVALID_ARG;
+  if (w->layout != MOE_LAYOUT_CANONICAL && w->layout != MOE_LAYOUT_PACKED) return MOE_ERR_INVALID_ARG;
   if ((st = device_check()) != MOE_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -247,6 +271,7 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   g.w_codes = w->w13;
   g.w_sc = w->w13_sc;
   g.w_gs = w->gs;
+  g.packed = w->layout == MOE_LAYOUT_PACKED;
   g.offsets = b.offsets;
   g.sorted = b.sorted;
   g.worklist = b.worklist;

@@ -76,6 +76,19 @@ __device__ inline void load_frag(Frag4& f, const uint8_t* row, const uint8_t* sc
   const uint8_t* s = sc_row + k0 / 16 + 2 * g;
   f.sc = (uint32_t)s[0] | ((uint32_t)s[1] << 8);
 }
+// Packed layout: tile = 16 rows x 128 columns in MFMA lane order; `tile`
+// points at lane 0 of the row group's step-0 tile, sc at its scales.
+__device__ inline void load_frag_packed(Frag8& f, const uint8_t* tile, const uint8_t* sc, int step, int lane) {
+  const uint8_t* t = tile + (size_t)step * 2048 + 16 * lane;
+  f.lo = *reinterpret_cast<const uint4*>(t);
+  f.hi = *reinterpret_cast<const uint4*>(t + 1024);
+  f.sc = sc[step * 64 + lane];
+}
+__device__ inline void load_frag_packed(Frag4& f, const uint8_t* tile, const uint8_t* sc, int step, int lane) {
+  f.q = *reinterpret_cast<const uint4*>(tile + (size_t)step * 1024 + 16 * lane);
+  f.sc = *reinterpret_cast<const uint16_t*>(sc + step * 128 + 2 * lane);
+}
+
 __device__ inline void zero_frag(Frag8& f) {
   f.lo = make_uint4(0, 0, 0, 0);
   f.hi = f.lo;
@@ -148,7 +161,7 @@ __device__ inline void step_compute(const Frag* fa, const Frag* fb, v4f (*acc)[N
 // NST > 0: every wave runs exactly NST k steps (K = 128 * NST * KS), fully
 // unrolled with no branch in the step sequence; NST == 0: any K, runtime
 // trip counts.
-template <int FMT, int STAGE, int MS, int PF, int NST>
+template <int FMT, int STAGE, int MS, int PF, int NST, bool PACKED>
 __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
   constexpr int KS = STAGE == 0 ? 4 : 2, NS = 4 / KS;
   constexpr int TM = 16 * MS, BN = 64, NCG = 4 / NS;
@@ -183,8 +196,14 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
       n = (cg < 2 ? 0 : a.F) + blockIdx.x * 32 + 16 * (cg & 1) + r;
     else
       n = blockIdx.x * BN + 16 * cg + r;
-    brow[c] = wexp + (size_t)n * row_bytes;
-    bsrow[c] = wsexp + (size_t)n * sc_bytes;
+    if (PACKED) {   // the row group's first tile (all K steps of a group are contiguous)
+      const size_t tiles = (size_t)((n - r) / 16) * (K / 128);
+      brow[c] = wexp + tiles * (FMT == 2 ? 2048 : 1024);
+      bsrow[c] = wsexp + tiles * (FMT == 2 ? 64 : 128);
+    } else {
+      brow[c] = wexp + (size_t)n * row_bytes;
+      bsrow[c] = wsexp + (size_t)n * sc_bytes;
+    }
   }
 
   if (threadIdx.x < TM) {
@@ -217,7 +236,10 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
   Frag fa[PF][MS], fb[PF][NCG];
   auto issue = [&](int step, Frag* A, Frag* B) {
 #pragma unroll
-    for (int c = 0; c < NCG; c++) load_frag(B[c], brow[c], bsrow[c], step * 128, g);
+    for (int c = 0; c < NCG; c++) {
+      if (PACKED) load_frag_packed(B[c], brow[c], bsrow[c], step, lane);
+      else load_frag(B[c], brow[c], bsrow[c], step * 128, g);
+    }
 #pragma unroll
     for (int i = 0; i < MS; i++) load_frag(A[i], arow[i], asrow[i], step * 128, g);
   };
@@ -300,8 +322,15 @@ static int launch_any(const GemmArgs& a, int stage, hipStream_t stream) {
   // Inkling 2 Small: H = 4608 gives 36 k steps = 4 waves x 9 (gate/up);
   // F = 2304 gives 18 = 2 waves x 9 (down).
   const bool fast = stage == 0 ? a.H == 128 * 9 * 4 : a.F == 128 * 9 * 2;
-#define MOE_LAUNCH(FMT, ST, MS, NST) \
-  hipLaunchKernelGGL((k_expert_gemm<FMT, ST, MS, (FMT == 1 ? 3 : 2), NST>), grid, block, 0, stream, a)
+#define MOE_LAUNCH(FMT, ST, MS, NST)                                                                \
+  do {                                                                                              \
+    if (a.packed)                                                                                   \
+      hipLaunchKernelGGL((k_expert_gemm<FMT, ST, MS, (FMT == 1 ? 3 : 2), NST, true>), grid, block, 0, \
+                         stream, a);                                                                \
+    else                                                                                            \
+      hipLaunchKernelGGL((k_expert_gemm<FMT, ST, MS, (FMT == 1 ? 3 : 2), NST, false>), grid, block, 0, \
+                         stream, a);                                                                \
+  } while (0)
 #define MOE_LAUNCH_N(FMT, ST, MS)                  \
   do {                                             \
     if (fast) MOE_LAUNCH(FMT, ST, MS, 9);          \

@@ -46,6 +46,7 @@ struct GemmArgs {
   const uint8_t* w_codes;
   const uint8_t* w_sc;
   const float* w_gs;       // [E_local][3] (NVFP4)
+  int packed;              // weights in the packed tile layout
   // routing
   const int32_t* offsets;  // [E_local+1]
   const int32_t* sorted;   // [P] pair ids in expert order
@@ -61,6 +62,11 @@ struct GemmArgs {
 int gemm_tile_m(int T, int k, int E_local);
 int launch_gemm_gateup(const GemmArgs& a, hipStream_t stream);
 int launch_gemm_down(const GemmArgs& a, hipStream_t stream);
+
+// Repack nmat canonical [N][K] matrices (codes + scales) into the packed
+// tile layout (moe_prepare_weights).
+int launch_pack(int fmt, const uint8_t* codes, const uint8_t* scales, long nmat, int N, int K,
+                uint8_t* pcodes, uint8_t* pscales, hipStream_t stream);
 
 int launch_combine(const float* y, const int32_t* pos, const float* w, int T, int k, int H,
                    uint16_t* out, hipStream_t stream);

@@ -101,7 +101,13 @@ typedef struct moe_config {
   int32_t max_tokens;         /* largest T the workspace is sized for */
 } moe_config;
 
-/* Expert weights of the LOCAL experts, canonical layout, expert-major.
+/* Byte order of the expert weight arrays. */
+enum moe_layout {
+  MOE_LAYOUT_CANONICAL = 0, /* row-major, as a checkpoint stores it (below) */
+  MOE_LAYOUT_PACKED = 1     /* the same bytes permuted by moe_prepare_weights */
+};
+
+/* Expert weights of the LOCAL experts, expert-major.  Canonical layout:
  * For local expert i (global id expert_begin + i), with H = hidden, F = ffn:
  *  NVFP4: w13    [i][2F][H/2]   E2M1 codes; rows 0..F-1 gate, F..2F-1 up
  *         w13_sc [i][2F][H/16]  E4M3 block scales
@@ -110,13 +116,17 @@ typedef struct moe_config {
  *         gs     [i][3]         fp32 scales of gate, up, down
  *  MXFP8: w13    [i][2F][H]     E4M3 codes; w13_sc [i][2F][H/32] E8M0
  *         w2     [i][H][F]      E4M3 codes; w2_sc  [i][H][F/32]  E8M0
- *         gs     unused (may be NULL). */
+ *         gs     unused (may be NULL).
+ * The packed layout holds exactly the same arrays (same sizes, same gs) with
+ * the bytes of every 16-row x 128-column tile reordered so that each
+ * wavefront load of the expert GEMMs reads one contiguous kilobyte. */
 typedef struct moe_expert_weights {
   const uint8_t* w13;
   const uint8_t* w13_sc;
   const uint8_t* w2;
   const uint8_t* w2_sc;
   const float* gs;
+  int32_t layout;           /* enum moe_layout */
 } moe_expert_weights;
 
 /* Optional per-stage timing: events[2*s] is recorded before stage s and
@@ -188,6 +198,27 @@ int moe_route(const moe_config* cfg, const void* x, int32_t T, const void* w_rou
 int moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t T,
                  int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* One-time repack of the local experts' weights from the canonical layout
+ * into the packed layout the expert GEMMs stream fastest (load-time work,
+ * like a serving engine's weight loading; no value changes: every code and
+ * scale byte moves, none is re-encoded).  src: canonical arrays; dst: arrays
+ * of the same sizes (host struct with device pointers, owned by the caller;
+ * must not overlap src).  dst->gs is not written (the fp32 scales keep their
+ * layout; point dst->gs at src->gs).  Sets dst->layout = MOE_LAYOUT_PACKED.
+ * Tile (g, s) of a matrix with K columns covers rows 16g..16g+15 and
+ * columns 128s..128s+127; tiles are stored in (g, s) order, each in the
+ * lane order of the MFMA operand (lane l = row 16g + l%16, column group
+ * l/16):
+ *  NVFP4 codes: 1024 B per tile, lane l's 16 bytes at 16 l (its 32 codes
+ *         at columns 128s + 32(l/16)); scales: 128 B per tile, lane l's two
+ *         E4M3 bytes at 2 l.
+ *  MXFP8 codes: 2048 B per tile, lane l's bytes for columns
+ *         128s + 16(l/16) + [0,16) at 16 l and for columns
+ *         128s + 64 + 16(l/16) + [0,16) at 1024 + 16 l; scales: 64 B per
+ *         tile, lane l's E8M0 byte (block 4s + l/16) at l. */
+int moe_prepare_weights(const moe_config* cfg, const moe_expert_weights* src, moe_expert_weights* dst,
+                        void* stream);
 
 /* The expert half of the layer for T tokens already routed (topk_ids /
  * topk_w from moe_route, or replayed from elsewhere: Miles docs section 5.3,

@@ -17,7 +17,7 @@ from _util import OUT_RTOL, inputs, lib_cfg, oracle_cfg, rel_err, stack_local, t
 pytestmark = pytest.mark.gpu
 
 
-def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None):
+def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None, layout="packed"):
     import torch
     x, wr, b = inputs(w, T)
     T = x.shape[0]
@@ -25,6 +25,8 @@ def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None):
     cfg = lib_cfg(bse, w, max_tokens=max_tokens or T, **kw)
     stacked, ews = stack_local(w, gain)
     wd = {k: to_dev(v) for k, v in stacked.items()}
+    if layout == "packed":
+        wd = bse.prepare_weights(cfg, wd)
     ws = bse.workspace(cfg)
     ids = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
     tw = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
@@ -105,3 +107,14 @@ def test_inkling_decode_sampled(gpu_lib, key, ntok):
     # determinism: a second run is bit-identical
     r2 = run_layer(gpu_lib, w)
     assert np.array_equal(r2["out"], r["out"])
+
+
+@pytest.mark.parametrize("key", ["tiny", "mid_nvfp4", "mid_mxfp8", "ep_nvfp4", "decode_nvfp4", "decode_mxfp8"])
+def test_packed_layout_matches_canonical_bit_exact(gpu_lib, key):
+    """moe_prepare_weights only permutes bytes: the layer output with packed
+    weights is bit-identical to the output with the canonical arrays."""
+    w = SMALL.get(key) or synth.WORKLOADS[key]
+    a = run_layer(gpu_lib, w, layout="canonical")
+    b = run_layer(gpu_lib, w, layout="packed")
+    assert np.array_equal(a["ids"], b["ids"])
+    assert np.array_equal(a["out"], b["out"])
