@@ -72,6 +72,21 @@ def upload_weights(w, bse_cfg):
     return dev, per_expert
 
 
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes (fetch + write) per launch of `kernel` ("gate_up" / "down")
+    recorded from rocprofv3 counters in profiles/traffic.json, if the GEMM
+    source has not changed since; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload)
+    src = open(os.path.join(ROOT, "block_scaled_expert_amd", "csrc", "gemm.hip"), "rb").read()
+    if not rec or rec.get("gemm_hip_sha256") != hashlib.sha256(src).hexdigest() or kernel not in rec:
+        return None
+    return rec[kernel]["fetch_bytes"] + rec[kernel]["write_bytes"]
+
+
 def cpu_baseline(w, x, wr, b, budget_s: float = 20.0):
     """The oracle (as it stands) on a bounded sample: whole layer outputs for a
     few tokens, routing included, using all host threads for BLAS."""
@@ -200,14 +215,17 @@ def main() -> int:
     decode = w.key.startswith("decode") or w.key == "tiny"
     if decode or w.key.startswith("ep8"):
         achieved = active * w13_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9
+        tr = measured_traffic(w.key, "gate_up") if args.layout == "packed" else None
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
+                "traffic_over_algorithmic": None if tr is None else round(tr / (active * w13_bytes), 4),
                 "kernel": "k_expert_gemm gate/up", "per_launch": f"{active} experts x {w13_bytes} B (w13 codes + scales)"}
     else:
         issued = MFMA_ISSUED[w.fmt]
         achieved = flops_gu / (stage_ms["gate_up"] * 1e-3) / 1e12
+        tr = measured_traffic(w.key, "gate_up") if args.layout == "packed" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[issued], "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_PEAK_TFLOPS[issued], 4), "traffic": None,
+                "frac": round(achieved / MFMA_PEAK_TFLOPS[issued], 4), "traffic": tr,
                 "kernel": "k_expert_gemm gate/up", "mfma_issued": issued,
                 "frac_of_fp8_peak": round(achieved / MFMA_PEAK_TFLOPS["fp8"], 4),
                 "frac_of_fp4_peak": round(achieved / MFMA_PEAK_TFLOPS["fp4"], 4),

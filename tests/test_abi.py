@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/moe.h declares, and the host-side argument checks return the
+documented statuses before anything touches a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_scaled_expert_amd as bse
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bse.LIB_PATH):
+        from block_scaled_expert_amd import build
+        build.build()
+    return bse.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_quantize_act", "moe_forward", "moe_dispatch", "moe_prepare_weights",
+              "moe_workspace_size", "moe_status_string", "moe_check_arch", "moe_validate_config"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", bse.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(moe_\w+)", out))
+    assert set(declared_functions()) <= exported
+    assert set(bse.EXPORTED) <= exported
+
+
+def test_check_arch(lib):
+    assert bse.check_arch("gfx950") == 0
+    assert bse.check_arch("gfx950:sramecc+:xnack-") == 0
+    for bad in ("gfx942", "gfx9500", "gfx90a", "", "gfx95"):
+        assert bse.check_arch(bad) == -2, bad
+    assert lib.moe_check_arch(None) == -1
+
+
+def test_status_strings(lib):
+    for st in range(0, -8, -1):
+        assert bse.status_string(st) != "unknown status"
+    assert bse.status_string(-99) == "unknown status"
+
+
+def _cfg(**kw):
+    base = dict(hidden=4608, ffn=2304, num_experts=384, top_k=8, fmt="nvfp4", max_tokens=64)
+    base.update(kw)
+    return bse.Config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    ({"hidden": 4600}, -1), ({"ffn": 100}, -1), ({"num_experts": 0}, -1), ({"num_experts": 2000}, -1),
+    ({"top_k": 0}, -1), ({"top_k": 33}, -1), ({"num_experts": 4, "top_k": 5}, -1),
+    ({"expert_begin": 380, "num_local_experts": 8}, -1), ({"num_local_experts": 0}, -1),
+    ({"cap_form": 7}, -1), ({"cap": 0.0}, -1), ({"cap": 0.0, "cap_form": 3}, 0),
+    ({"max_tokens": -1}, -1), ({"max_tokens": 1 << 22}, -1),
+])
+def test_validate_config(lib, kw, status):
+    cc = _cfg(**kw).c()
+    assert lib.moe_validate_config(ctypes.byref(cc)) == status
+
+
+def test_unsupported_format(lib):
+    cc = _cfg().c()
+    cc.fmt = 3
+    assert lib.moe_validate_config(ctypes.byref(cc)) == -5
+
+
+def test_workspace_size_grows_with_tokens(lib):
+    sizes = [bse.workspace_size(_cfg(max_tokens=t)) for t in (0, 1, 64, 192, 16384)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    # the fp32 SwiGLU output and expert outputs dominate: P*(F+H)*4 bytes
+    assert sizes[-1] >= 16384 * 8 * (2304 + 4608) * 4
+
+
+def test_host_checks_before_device(lib):
+    """Argument errors come back without a GPU (nothing is enqueued)."""
+    cc = _cfg(max_tokens=64).c()
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_size(ctypes.byref(cc), None) == -1
+    assert lib.moe_workspace_size(ctypes.byref(cc), ctypes.byref(n)) == 0
+    # too many tokens
+    assert lib.moe_route(ctypes.byref(cc), None, 65, None, None, None, None, None, None, 0, None) == -4
+    assert lib.moe_forward(ctypes.byref(cc), None, 65, None, None, None, None, None, 0, None, None) == -4
+    # null / misaligned / small workspace
+    assert lib.moe_route(ctypes.byref(cc), None, 8, None, None, None, None, None, None, 0, None) == -1
+    assert lib.moe_forward(ctypes.byref(cc), None, 8, None, None, None, None, ctypes.c_void_p(0x1001),
+                           n.value, None, None) == -1
+    assert lib.moe_forward(ctypes.byref(cc), None, 8, None, None, None, None, ctypes.c_void_p(0x1000),
+                           n.value - 1, None, None) == -3
+    assert lib.moe_dispatch(ctypes.byref(cc), None, 8, None, None, None, ctypes.c_void_p(0x1000), n.value,
+                            None) == -1
+    # zero tokens is a no-op that needs no device
+    assert lib.moe_forward(ctypes.byref(cc), None, 0, None, None, None, None, ctypes.c_void_p(0x1000), n.value,
+                           None, None) == 0
+    # bad quantize arguments
+    assert lib.moe_quantize_act(1, 0, None, 4, 48, None, None, None, None) == -1   # cols % 32
+    assert lib.moe_quantize_act(3, 0, None, 4, 64, None, None, None, None) == -5   # format
+    assert lib.moe_quantize_act(1, 2, None, 4, 64, None, None, None, None) == -1   # dtype
+    assert lib.moe_quantize_act(1, 0, None, 0, 64, None, None, None, None) == 0    # nothing to do
+    # weights: bad layout value / canonical source required
+    w = bse.CWeights(1, 1, 1, 1, 1, 5)
+    assert lib.moe_prepare_weights(ctypes.byref(cc), ctypes.byref(w), ctypes.byref(bse.CWeights()), None) == -1
