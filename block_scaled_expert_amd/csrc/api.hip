@@ -246,7 +246,8 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   record(events, 2 * MOE_STAGE_QUANT_X + 1, s);
 
   // 2. dispatch + tile list
-  const int tile_m = gemm_tile_m(T, k, EL);
+  int tile_m = gemm_tile_m(T, k, c->num_experts);
+  if (tile_m == 128 && !gemm_big_supported(H, F)) tile_m = 64;
   DispatchBufs b;
   b.counts = at<int32_t>(ws, L.counts);
   b.offsets = at<int32_t>(ws, L.offsets);

@@ -310,13 +310,15 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
   }
 }
 
-int gemm_tile_m(int T, int k, int E_local) {
-  // average rows per local expert decides the rows per work-list entry
-  const long avg = (long)T * k / (E_local > 0 ? E_local : 1);
-  return avg <= 2 ? 16 : (avg <= 24 ? 32 : 64);
+int gemm_tile_m(int T, int k, int E) {
+  // expected rows per expert (uniform routing) picks the rows per work-list
+  // entry; 128-row entries go to the LDS-tiled kernel (gemm_big.hip)
+  const long avg = (long)T * k / (E > 0 ? E : 1);
+  return avg <= 2 ? 16 : avg <= 24 ? 32 : avg <= 48 ? 64 : 128;
 }
 
 static int launch_any(const GemmArgs& a, int stage, hipStream_t stream) {
+  if (a.tile_m == 128) return launch_gemm_big(a, stage, stream);
   const dim3 block(256);
   const dim3 grid(stage == 0 ? a.F / 32 : a.H / 64, a.max_tiles);
   // Inkling 2 Small: H = 4608 gives 36 k steps = 4 waves x 9 (gate/up);

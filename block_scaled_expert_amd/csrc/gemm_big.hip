@@ -1,0 +1,353 @@
+// Grouped expert GEMMs for many rows per expert (prefill chunks, an expert-
+// parallel share).  The layer and format sources are those of gemm.hip
+// (SGLang cookbook "Inkling-2-Small" section 2, "MegaMoE" and "Checkpoints";
+// Miles docs section 5.3).
+//
+// Workgroup: 8 waves, tile of 128 rows (a dispatch work-list entry with
+// tile_m = 128) x 256 weight rows, k step 128.  Waves form 2 (rows) x 4
+// (weight rows); each owns a 64 x 64 block of sixteen 16x16 MFMA tiles.
+//  - The activation tile of each k step is staged through LDS once per
+//    workgroup (double-buffered, one barrier per step) and shared by the four
+//    waves of each row half.  NVFP4 activations are expanded to f16 (code *
+//    block scale, exact) while they are written to LDS, so the expansion is
+//    paid once per workgroup; MXFP8 activations stay E4M3 with their E8M0
+//    scales.
+//  - Each wave streams its own 64 weight rows straight from HBM into MFMA
+//    operand registers through a ring of PF k steps (the packed tile layout:
+//    one contiguous kilobyte per wavefront load; the canonical layout works
+//    too, with 64-byte row pieces).  NVFP4 weight fragments are expanded in
+//    registers as in the decode kernel.
+// Each weight element is fetched once per 128 rows of an expert; the
+// activation tile once per 256 weight rows.
+#include <type_traits>
+
+#include "moe_common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int BM = 128, BNW = 256, WAVES = 8;
+
+__device__ inline v8h dq8(uint32_t word, v2h sig2) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 0) * sig2;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 1) * sig2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 2) * sig2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 3) * sig2;
+  return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+// two E4M3 bytes -> f16 pair {sigma0, sigma1} * 2^-8 (field move, see gemm.hip)
+__device__ inline v2h sig2_of(uint32_t w) {
+  const uint32_t b = ((w & 0x7Fu) << 7) | ((w & 0x80u) << 8) | ((w & 0x7F00u) << 15) | ((w & 0x8000u) << 16);
+  return __builtin_bit_cast(v2h, b);
+}
+
+struct BFrag4 {   // NVFP4 weight fragment: 16 B codes + 2 scale bytes
+  uint4 q;
+  uint32_t sc;
+};
+struct BFrag8 {   // MXFP8 weight fragment: 32 B codes + 1 scale byte
+  uint4 lo, hi;
+  uint32_t sc;
+};
+
+// Activation staging: one thread's quarter of one row for one k step.
+struct AStage4 {
+  uint4 q;        // 32 codes (column group g = quarter)
+  uint32_t sc;    // their two scale bytes
+};
+struct AStage8 {
+  uint4 lo, hi;   // 32 bytes of the 128-byte step
+  uint32_t sc;    // scale byte of this quarter
+};
+
+// LDS bytes per buffer: NVFP4 8 row tiles x 4 KB of f16; MXFP8 8 x (2 KB + 64 B).
+template <int FMT>
+constexpr int abuf_bytes() {
+  return FMT == 1 ? 8 * 4096 : 8 * (2048 + 64);
+}
+
+}  // namespace
+
+template <int FMT, int STAGE, bool PACKED, int PF>
+__global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
+  typedef typename std::conditional<FMT == 2, BFrag8, BFrag4>::type BFrag;
+  typedef typename std::conditional<FMT == 2, AStage8, AStage4>::type AStage;
+  constexpr int ABUF = abuf_bytes<FMT>();
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int tok[BM];
+
+  const int tile = blockIdx.y;
+  if (tile >= a.ntiles[0]) return;
+  const int el = a.worklist[2 * tile], m0 = a.worklist[2 * tile + 1];
+  const int row0 = a.offsets[el] + m0;
+  const int rows = min(BM, a.offsets[el + 1] - row0);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int r = lane & 15, g = lane >> 4;
+  const int K = STAGE == 0 ? a.H : a.F;
+  const int NS = K / 128;
+  const int NW = STAGE == 0 ? 2 * a.F : a.H;
+  const int row_bytes = FMT == 2 ? K : K / 2;
+  const int sc_bytes = FMT == 2 ? K / 32 : K / 16;
+  const uint8_t* wexp = a.w_codes + (size_t)el * NW * row_bytes;
+  const uint8_t* wsexp = a.w_sc + (size_t)el * NW * sc_bytes;
+
+  if (tid < BM) tok[tid] = tid < rows ? (STAGE == 0 ? a.sorted[row0 + tid] / a.k : row0 + tid) : -1;
+  __syncthreads();
+
+  // ---- activation staging: row ar = tid/4, quarter aq = tid%4 -------------
+  const int ar = tid >> 2, aq = tid & 3;
+  const int at = tok[ar] >= 0 ? tok[ar] : tok[0];     // rows past the tile: outputs discarded
+  const uint8_t* acode = a.a_codes + (size_t)at * row_bytes;
+  const uint8_t* asc = a.a_sc + (size_t)at * sc_bytes;
+  auto aload = [&](int s, AStage& st) {
+    if constexpr (FMT == 1) {
+      st.q = *reinterpret_cast<const uint4*>(acode + s * 64 + 16 * aq);
+      st.sc = *reinterpret_cast<const uint16_t*>(asc + s * 8 + 2 * aq);
+    } else {
+      const uint4* p = reinterpret_cast<const uint4*>(acode + s * 128 + 32 * aq);
+      st.lo = p[0];
+      st.hi = p[1];
+      st.sc = asc[s * 4 + aq];
+    }
+  };
+  auto astore = [&](int buf, const AStage& st) {
+    uint8_t* A = lds + buf * ABUF;
+    const int f = ar >> 4, rr = ar & 15;
+    if constexpr (FMT == 1) {
+      // column group g = aq of row rr is lane rr + 16 aq; MFMA part j takes
+      // its elements 8j..8j+7; stored [tile f][part j][lane], f16 x 8 each
+      const v2h sp = sig2_of(st.sc);
+      const v2h s0 = v2h{sp[0], sp[0]}, s1 = v2h{sp[1], sp[1]};
+      uint8_t* base = A + f * 4096 + (rr + 16 * aq) * 16;
+      *reinterpret_cast<v8h*>(base + 0 * 1024) = dq8(st.q.x, s0);
+      *reinterpret_cast<v8h*>(base + 1 * 1024) = dq8(st.q.y, s0);
+      *reinterpret_cast<v8h*>(base + 2 * 1024) = dq8(st.q.z, s1);
+      *reinterpret_cast<v8h*>(base + 3 * 1024) = dq8(st.q.w, s1);
+    } else {
+      // bytes [32 aq, +32) of the row's step are column groups 2(aq%2) and
+      // 2(aq%2)+1: their first halves for aq < 2, second halves for aq >= 2
+      const int h = aq >> 1, g0 = 2 * (aq & 1);
+      uint8_t* T = A + f * 2112;
+      *reinterpret_cast<uint4*>(T + 1024 * h + (rr + 16 * g0) * 16) = st.lo;
+      *reinterpret_cast<uint4*>(T + 1024 * h + (rr + 16 * (g0 + 1)) * 16) = st.hi;
+      T[2048 + rr + 16 * aq] = (uint8_t)st.sc;
+    }
+  };
+
+  // ---- weight fragments of this wave (4 column groups of 16 weight rows) ---
+  const uint8_t* brow[4];
+  const uint8_t* bsrow[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    int n0;   // first weight row of column group c
+    if (STAGE == 0)   // c = 0,1: gate rows; c = 2,3: the matching up rows
+      n0 = (c < 2 ? 0 : a.F) + blockIdx.x * 128 + 32 * wn + 16 * (c & 1);
+    else
+      n0 = blockIdx.x * BNW + 64 * wn + 16 * c;
+    if (PACKED) {
+      const size_t t0 = (size_t)(n0 / 16) * NS;
+      brow[c] = wexp + t0 * (FMT == 2 ? 2048 : 1024);
+      bsrow[c] = wsexp + t0 * (FMT == 2 ? 64 : 128);
+    } else {
+      brow[c] = wexp + (size_t)(n0 + r) * row_bytes;
+      bsrow[c] = wsexp + (size_t)(n0 + r) * sc_bytes;
+    }
+  }
+  auto bload = [&](int s, BFrag* B) {
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      if constexpr (FMT == 1) {
+        if (PACKED) {
+          B[c].q = *reinterpret_cast<const uint4*>(brow[c] + (size_t)s * 1024 + 16 * lane);
+          B[c].sc = *reinterpret_cast<const uint16_t*>(bsrow[c] + s * 128 + 2 * lane);
+        } else {
+          B[c].q = *reinterpret_cast<const uint4*>(brow[c] + s * 64 + 16 * g);
+          const uint8_t* sp = bsrow[c] + s * 8 + 2 * g;
+          B[c].sc = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+        }
+      } else {
+        if (PACKED) {
+          const uint8_t* t = brow[c] + (size_t)s * 2048 + 16 * lane;
+          B[c].lo = *reinterpret_cast<const uint4*>(t);
+          B[c].hi = *reinterpret_cast<const uint4*>(t + 1024);
+          B[c].sc = bsrow[c][s * 64 + lane];
+        } else {
+          B[c].lo = *reinterpret_cast<const uint4*>(brow[c] + s * 128 + 16 * g);
+          B[c].hi = *reinterpret_cast<const uint4*>(brow[c] + s * 128 + 64 + 16 * g);
+          B[c].sc = bsrow[c][s * 4 + g];
+        }
+      }
+    }
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int c = 0; c < 4; c++) acc[i][c] = v4f{0, 0, 0, 0};
+
+  auto compute = [&](int buf, const BFrag* B) {
+    const uint8_t* A = lds + buf * ABUF;
+    if constexpr (FMT == 1) {
+      v2h bs[4][2];
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const v2h sp = sig2_of(B[c].sc);
+        bs[c][0] = v2h{sp[0], sp[0]};
+        bs[c][1] = v2h{sp[1], sp[1]};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        v8h bv[4];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const uint32_t w = j == 0 ? B[c].q.x : j == 1 ? B[c].q.y : j == 2 ? B[c].q.z : B[c].q.w;
+          bv[c] = dq8(w, bs[c][j >> 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const v8h av = *reinterpret_cast<const v8h*>(A + (4 * wm + i) * 4096 + j * 1024 + lane * 16);
+#pragma unroll
+          for (int c = 0; c < 4; c++)
+            acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[c], acc[i][c], 0, 0, 0);
+        }
+      }
+    } else {
+      v8i bv[4];
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        bv[c] = v8i{(int)B[c].lo.x, (int)B[c].lo.y, (int)B[c].lo.z, (int)B[c].lo.w,
+                    (int)B[c].hi.x, (int)B[c].hi.y, (int)B[c].hi.z, (int)B[c].hi.w};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const uint8_t* T = A + (4 * wm + i) * 2112;
+        const uint4 lo = *reinterpret_cast<const uint4*>(T + 16 * lane);
+        const uint4 hi = *reinterpret_cast<const uint4*>(T + 1024 + 16 * lane);
+        const v8i av = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const int as = T[2048 + lane];
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+          acc[i][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[c], acc[i][c], 0, 0, 0, as, 0,
+                                                                       (int)B[c].sc);
+      }
+    }
+  };
+
+  // ---- main loop: PF steps of weights and activations in flight ----------
+  // NS is a multiple of PF; slot j holds the steps congruent to j mod PF.
+  // No load sits under a branch (see gemm.hip); past the end a step is
+  // re-read, harmlessly.
+  BFrag bring[PF][4];
+  AStage ast[PF];
+#pragma unroll
+  for (int j = 0; j < PF; j++) {
+    bload(min(j, NS - 1), bring[j]);
+    aload(min(j, NS - 1), ast[j]);
+  }
+  astore(0, ast[0]);
+  aload(min(PF, NS - 1), ast[0]);
+  __syncthreads();
+  for (int s0 = 0; s0 < NS; s0 += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; j++) {
+      const int step = s0 + j;
+      compute(step & 1, bring[j]);
+      bload(min(step + PF, NS - 1), bring[j]);
+      // the next step's activations sit in slot (j+1)%PF; refill it after
+      astore((step + 1) & 1, ast[(j + 1) % PF]);
+      aload(min(step + 1 + PF, NS - 1), ast[(j + 1) % PF]);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue straight from registers -----------------------------------
+  // acc reg q of lane l in tile (i, c): row 64 wm + 16 i + 4 (l/16) + q,
+  // weight row (column) 16 * (group c) + l%16.
+  const int cl = lane & 15, g4 = lane >> 4;
+  if (STAGE == 0) {
+    const float inv_c = 1.0f / a.cap;
+    const float wg = FMT == 1 ? a.w_gs[3 * el + 0] : 1.0f;
+    const float wu = FMT == 1 ? a.w_gs[3 * el + 1] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int m = 64 * wm + 16 * i + 4 * g4 + q;
+        if (m >= rows) continue;
+        const float ga = FMT == 1 ? a.a_gs[tok[m]] : 1.0f;
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+          float gv = acc[i][c][q], uv = acc[i][c + 2][q];
+          if (FMT == 1) {
+            gv = (gv * ga) * wg;
+            uv = (uv * ga) * wu;
+          }
+          const int col = blockIdx.x * 128 + 32 * wn + 16 * c + cl;
+          a.out[(size_t)(row0 + m) * a.F + col] = cap_swiglu(gv, uv, a.cap_form, a.cap, inv_c);
+        }
+      }
+  } else {
+    const float wd = FMT == 1 ? a.w_gs[3 * el + 2] : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int m = 64 * wm + 16 * i + 4 * g4 + q;
+        if (m >= rows) continue;
+        const float ha = FMT == 1 ? a.a_gs[row0 + m] : 1.0f;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          float yv = acc[i][c][q];
+          if (FMT == 1) yv = (yv * ha) * wd;
+          a.out[(size_t)(row0 + m) * a.H + blockIdx.x * BNW + 64 * wn + 16 * c + cl] = yv;
+        }
+      }
+  }
+}
+
+namespace {
+
+template <int FMT, int ST, bool PK, int PF>
+void launch_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  const size_t lds = 2 * abuf_bytes<FMT>();
+  static bool done = false;   // dynamic LDS above 64 KiB must be allowed once
+  if (!done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm_big<FMT, ST, PK, PF>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    done = true;
+  }
+  hipLaunchKernelGGL((k_expert_gemm_big<FMT, ST, PK, PF>), grid, dim3(WAVES * 64), lds, stream, a);
+}
+
+template <int FMT, int ST, bool PK>
+void launch_pf(const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  const int ns = (ST == 0 ? a.H : a.F) / 128;
+  if (ns % 2 == 0) launch_one<FMT, ST, PK, 2>(a, grid, stream);
+  else launch_one<FMT, ST, PK, 1>(a, grid, stream);
+}
+
+}  // namespace
+
+bool gemm_big_supported(int H, int F) { return H % BNW == 0 && F % 128 == 0; }
+
+int launch_gemm_big(const GemmArgs& a, int stage, hipStream_t stream) {
+  const dim3 grid(stage == 0 ? a.F / 128 : a.H / BNW, a.max_tiles);
+#define MOE_BIG(FMT, ST)                                     \
+  do {                                                       \
+    if (a.packed) launch_pf<FMT, ST, true>(a, grid, stream); \
+    else launch_pf<FMT, ST, false>(a, grid, stream);         \
+  } while (0)
+  if (a.fmt == 2) {
+    if (stage == 0) MOE_BIG(2, 0); else MOE_BIG(2, 1);
+  } else {
+    if (stage == 0) MOE_BIG(1, 0); else MOE_BIG(1, 1);
+  }
+#undef MOE_BIG
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace moe

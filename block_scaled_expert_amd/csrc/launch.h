@@ -53,13 +53,17 @@ struct GemmArgs {
   const int32_t* worklist; // [2*max_tiles]
   const int32_t* ntiles;   // [1]
   int max_tiles;           // grid.y: an upper bound of *ntiles
-  int tile_m;              // rows per work-list entry (16, 32 or 64; matches dispatch)
+  int tile_m;              // rows per work-list entry (16, 32, 64 or 128; matches dispatch)
   // epilogue
   int cap_form;
   float cap;
   float* out;              // gate/up: h [P][F]; down: y [P][H] (rows in sorted order)
 };
-int gemm_tile_m(int T, int k, int E_local);
+int gemm_tile_m(int T, int k, int E);
+// LDS-staged variant for 128-row work-list entries (gemm_big.hip); needs
+// H % 256 == 0 and F % 128 == 0.
+bool gemm_big_supported(int H, int F);
+int launch_gemm_big(const GemmArgs& a, int stage, hipStream_t stream);
 int launch_gemm_gateup(const GemmArgs& a, hipStream_t stream);
 int launch_gemm_down(const GemmArgs& a, hipStream_t stream);
 

@@ -96,12 +96,18 @@ def test_single_token_and_max_tokens_margin(gpu_lib):
     assert rel_err(r["out"], oracle_out(w, r)) <= OUT_RTOL
 
 
-@pytest.mark.parametrize("key,ntok", [("decode_nvfp4", 3), ("decode_mxfp8", 3)])
-def test_inkling_decode_sampled(gpu_lib, key, ntok):
+@pytest.mark.parametrize("key,ntok", [("decode_nvfp4", 3), ("decode_mxfp8", 3), ("ep8_mxfp8", 3),
+                                      ("prefill_nvfp4", 2)])
+def test_inkling_workloads_sampled(gpu_lib, key, ntok):
     w = synth.WORKLOADS[key]
     r = run_layer(gpu_lib, w)
     r["ews"] = None
-    toks = np.random.default_rng(1).choice(w.tokens, ntok, replace=False)
+    rng = np.random.default_rng(1)
+    if w.num_local is not None:   # tokens with at least one local expert
+        loc = (r["ids"] >= w.expert_begin) & (r["ids"] < w.expert_begin + w.num_local)
+        toks = rng.choice(np.nonzero(loc.any(1))[0], ntok, replace=False)
+    else:
+        toks = rng.choice(w.tokens, ntok, replace=False)
     ref = oracle_out(w, r, tokens=toks)
     assert rel_err(r["out"][toks], ref) <= OUT_RTOL
     # determinism: a second run is bit-identical
