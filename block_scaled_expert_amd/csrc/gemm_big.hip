@@ -18,7 +18,10 @@
 //    too, with 64-byte row pieces).  NVFP4 weight fragments are expanded in
 //    registers as in the decode kernel.
 // Each weight element is fetched once per 128 rows of an expert; the
-// activation tile once per 256 weight rows.
+// activation tile once per 256 weight rows.  Work items (row tile, weight
+// tile) are ordered so that the items one XCD runs back to back are
+// consecutive row tiles of the same weight tile: the hardware hands
+// workgroups to the 8 XCDs round-robin, and each XCD has its own L2.
 #include <type_traits>
 
 #include "moe_common.h"
@@ -78,8 +81,15 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int tok[BM];
 
-  const int tile = blockIdx.y;
-  if (tile >= a.ntiles[0]) return;
+  // XCD-aware order: work item L = (weight tile L / nt, row tile L % nt);
+  // consecutive items of one XCD are consecutive row tiles of one weight tile
+  const int nt = a.ntiles[0], nx = STAGE == 0 ? a.F / 128 : a.H / BNW;
+  const int items = nx * nt;
+  const int hw = blockIdx.x;
+  if (hw >= items) return;
+  const int q8 = items / 8, r8 = items % 8, xcd = hw % 8;
+  const int L = xcd * q8 + min(xcd, r8) + hw / 8;
+  const int tile = L % nt, bx = L / nt;
   const int el = a.worklist[2 * tile], m0 = a.worklist[2 * tile + 1];
   const int row0 = a.offsets[el] + m0;
   const int rows = min(BM, a.offsets[el + 1] - row0);
@@ -98,8 +108,11 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   if (tid < BM) tok[tid] = tid < rows ? (STAGE == 0 ? a.sorted[row0 + tid] / a.k : row0 + tid) : -1;
   __syncthreads();
 
-  // ---- activation staging: row ar = tid/4, quarter aq = tid%4 -------------
-  const int ar = tid >> 2, aq = tid & 3;
+  // ---- activation staging ------------------------------------------------
+  // Wave w stages row tile w: lane l takes row 16 w + l%16 and quarter
+  // aq = l/16 of the k step, so each LDS store of the wave is 1 KB contiguous
+  // (bank-conflict free).
+  const int ar = 16 * wave + (lane & 15), aq = lane >> 4;
   const int at = tok[ar] >= 0 ? tok[ar] : tok[0];     // rows past the tile: outputs discarded
   const uint8_t* acode = a.a_codes + (size_t)at * row_bytes;
   const uint8_t* asc = a.a_sc + (size_t)at * sc_bytes;
@@ -145,9 +158,9 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   for (int c = 0; c < 4; c++) {
     int n0;   // first weight row of column group c
     if (STAGE == 0)   // c = 0,1: gate rows; c = 2,3: the matching up rows
-      n0 = (c < 2 ? 0 : a.F) + blockIdx.x * 128 + 32 * wn + 16 * (c & 1);
+      n0 = (c < 2 ? 0 : a.F) + bx * 128 + 32 * wn + 16 * (c & 1);
     else
-      n0 = blockIdx.x * BNW + 64 * wn + 16 * c;
+      n0 = bx * BNW + 64 * wn + 16 * c;
     if (PACKED) {
       const size_t t0 = (size_t)(n0 / 16) * NS;
       brow[c] = wexp + t0 * (FMT == 2 ? 2048 : 1024);
@@ -286,7 +299,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
             gv = (gv * ga) * wg;
             uv = (uv * ga) * wu;
           }
-          const int col = blockIdx.x * 128 + 32 * wn + 16 * c + cl;
+          const int col = bx * 128 + 32 * wn + 16 * c + cl;
           a.out[(size_t)(row0 + m) * a.F + col] = cap_swiglu(gv, uv, a.cap_form, a.cap, inv_c);
         }
       }
@@ -303,7 +316,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
         for (int c = 0; c < 4; c++) {
           float yv = acc[i][c][q];
           if (FMT == 1) yv = (yv * ha) * wd;
-          a.out[(size_t)(row0 + m) * a.H + blockIdx.x * BNW + 64 * wn + 16 * c + cl] = yv;
+          a.out[(size_t)(row0 + m) * a.H + bx * BNW + 64 * wn + 16 * c + cl] = yv;
         }
       }
   }
@@ -335,7 +348,9 @@ void launch_pf(const GemmArgs& a, dim3 grid, hipStream_t stream) {
 bool gemm_big_supported(int H, int F) { return H % BNW == 0 && F % 128 == 0; }
 
 int launch_gemm_big(const GemmArgs& a, int stage, hipStream_t stream) {
-  const dim3 grid(stage == 0 ? a.F / 128 : a.H / BNW, a.max_tiles);
+  // one workgroup per work item, at most (weight tiles) x (work-list bound)
+  const int nx = stage == 0 ? a.F / 128 : a.H / BNW;
+  const dim3 grid(nx * a.max_tiles);
 #define MOE_BIG(FMT, ST)                                     \
   do {                                                       \
     if (a.packed) launch_pf<FMT, ST, true>(a, grid, stream); \
