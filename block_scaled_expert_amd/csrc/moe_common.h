@@ -104,17 +104,24 @@ __device__ inline float wave_sum(float v) {
 
 __device__ inline float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// tanh from one hardware exponential: tanh|x| = 1 - 2 / (e^{2|x|} + 1)
+// (relative error a few 1e-7; e^{2|x|} = inf gives exactly 1).
+__device__ inline float tanh_fast(float x) {
+  const float e = __expf(2.0f * fabsf(x));
+  return copysignf(1.0f - __fdividef(2.0f, e + 1.0f), x);
+}
+
 // Cap + SwiGLU on fp32 gate/up values (cap forms of enum moe_cap_form).
 __device__ inline float cap_swiglu(float g, float u, int form, float c, float inv_c) {
   if (form == 0) {            // soft cap on gate and up
-    g = c * tanhf(g * inv_c);
-    u = c * tanhf(u * inv_c);
+    g = c * tanh_fast(g * inv_c);
+    u = c * tanh_fast(u * inv_c);
   } else if (form == 1) {     // hard cap
     g = fminf(g, c);
     u = fminf(fmaxf(u, -c), c);
   }
-  float h = g / (1.0f + expf(-g)) * u;
-  if (form == 2) h = c * tanhf(h * inv_c);
+  float h = __fdividef(g, 1.0f + __expf(-g)) * u;
+  if (form == 2) h = c * tanh_fast(h * inv_c);
   return h;
 }
 
