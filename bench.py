@@ -129,6 +129,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each step as a captured HIP graph (launch overhead removed)")
     ap.add_argument("--layout", choices=["packed", "canonical"], default="packed",
                     help="expert weight layout (packed: moe_prepare_weights at load time)")
     args = ap.parse_args()
@@ -178,6 +180,20 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        # the whole step (route + forward) as one graph; no memsets are recorded
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_cap):
+            step()
+        torch.cuda.current_stream().wait_stream(s_cap)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
 
     # per-step stage events (recorded on the stream the kernels run on)
     nst = len(bse.STAGES)
@@ -191,11 +207,18 @@ def main() -> int:
     wall0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step(evs[i])
+        if graph is not None:
+            graph.replay()
+        else:
+            step(evs[i])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = start.elapsed_time(stop) / args.steps
+    if graph is not None:      # stage times from eager steps after the timed region
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
     stage_ms = {name: float(np.mean([evs[i][2 * s].elapsed_time(evs[i][2 * s + 1]) for i in range(args.steps)]))
                 for s, name in enumerate(bse.STAGES)}
 
@@ -239,6 +262,7 @@ def main() -> int:
         "data": "synthetic (seeded; expert weights drawn as codes)",
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "ffn": w.ffn,
                    "format": w.fmt, "local_experts": cfg.num_local, "weight_layout": args.layout,
+                   "launch": "hip_graph" if args.graph else "eager",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),

@@ -3,7 +3,8 @@
 // walk.  This is the "dispatch" stage that precedes both expert GEMMs in the
 // SGLang cookbook's MegaMoE description (section 2, "MegaMoE").
 //
-// Four launches, no floating point and no order-deciding atomics:
+// Batches of more than 4096 pairs take four launches (smaller ones one; see
+// k_disp_small), with no floating point and no order-deciding atomics:
 //   count   one workgroup per chunk of pairs: LDS histogram -> counts[c][e]
 //   scan    one workgroup per expert: exclusive scan of counts[*][e] over
 //           chunks (chunk order = pair order) -> per-chunk bases, totals[e]
@@ -128,8 +129,87 @@ __global__ __launch_bounds__(256) void k_disp_scatter(const int32_t* __restrict_
   }
 }
 
+// Small batches (P <= kSmallP pairs): the whole dispatch in one 1024-thread
+// workgroup -- LDS histogram, one scan over the experts (offsets and the tile
+// list), then passes of 1024 pairs ranked against the earlier pairs of the
+// same pass and the running per-expert counts of the passes before.
+constexpr int kSmallP = 4096;
+
+__global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__ ids, int P, int E_begin,
+                                                     int E_local, int tile_m, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
+                                                     int32_t* __restrict__ worklist,
+                                                     int32_t* __restrict__ ntiles) {
+  __shared__ int32_t cnt[1024], off[1024], toff[1024], run[1024], sub[1024];
+  const int i = threadIdx.x;
+  cnt[i] = 0;
+  run[i] = 0;
+  __syncthreads();
+  for (int p = i; p < P; p += 1024) {
+    const int e = ids[p] - E_begin;
+    if (e >= 0 && e < E_local) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  const int n = i < E_local ? cnt[i] : 0;
+  const int nt = (n + tile_m - 1) / tile_m;
+  off[i] = n;
+  toff[i] = nt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {        // inclusive scans of counts and tiles
+    const int a = i >= o ? off[i - o] : 0;
+    const int b = i >= o ? toff[i - o] : 0;
+    __syncthreads();
+    off[i] += a;
+    toff[i] += b;
+    __syncthreads();
+  }
+  const int excl = off[i] - n;
+  if (i < E_local) offsets[i] = excl;
+  if (i == 0) offsets[E_local] = off[1023];
+  if (i == 1023 && ntiles != nullptr) ntiles[0] = toff[1023];
+  if (worklist != nullptr && i < E_local) {
+    const int base = toff[i] - nt;
+    for (int j = 0; j < nt; j++) {
+      worklist[2 * (base + j)] = i;
+      worklist[2 * (base + j) + 1] = j * tile_m;
+    }
+  }
+  __syncthreads();
+  off[i] = excl;                               // exclusive offsets for the scatter
+  __syncthreads();
+  for (int p0 = 0; p0 < P; p0 += 1024) {
+    const int p = p0 + i;
+    int e = -1;
+    if (p < P) {
+      e = ids[p] - E_begin;
+      if (e < 0 || e >= E_local) e = -1;
+    }
+    sub[i] = e;
+    __syncthreads();
+    int rank = 0;
+    for (int j = 0; j < i; j++) rank += sub[j] == e ? 1 : 0;
+    if (p < P) {
+      if (e >= 0) {
+        const int q = off[e] + run[e] + rank;
+        if (sorted != nullptr) sorted[q] = p;
+        if (pos != nullptr) pos[p] = q;
+      } else if (pos != nullptr) {
+        pos[p] = -1;
+      }
+    }
+    __syncthreads();                           // every rank read run[] before it moves
+    if (e >= 0) atomicAdd(&run[e], 1);
+    __syncthreads();
+  }
+}
+
 int launch_dispatch(const int32_t* ids, int P, int E_begin, int E_local, int tile_m,
                     const DispatchBufs& b, hipStream_t stream) {
+  if (P <= kSmallP) {
+    hipLaunchKernelGGL(k_disp_small, dim3(1), dim3(1024), 0, stream, ids, P, E_begin, E_local, tile_m, b.offsets,
+                       b.sorted, b.pos, b.worklist, b.ntiles);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int chunk = dispatch_chunk(P > 0 ? P : 1);
   const int nchunks = P > 0 ? ceil_div(P, chunk) : 0;
   const size_t lds = (size_t)E_local * sizeof(int32_t);
