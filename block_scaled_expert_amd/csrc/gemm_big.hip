@@ -47,21 +47,21 @@ __device__ inline v2h sig2_of(uint32_t w) {
 }
 
 struct BFrag4 {   // NVFP4 weight fragment: 16 B codes + 2 scale bytes
-  uint4 q;
+  v4u q;
   uint32_t sc;
 };
 struct BFrag8 {   // MXFP8 weight fragment: 32 B codes + 1 scale byte
-  uint4 lo, hi;
+  v4u lo, hi;
   uint32_t sc;
 };
 
 // Activation staging: one thread's quarter of one row for one k step.
 struct AStage4 {
-  uint4 q;        // 32 codes (column group g = quarter)
+  v4u q;        // 32 codes (column group g = quarter)
   uint32_t sc;    // their two scale bytes
 };
 struct AStage8 {
-  uint4 lo, hi;   // 32 bytes of the 128-byte step
+  v4u lo, hi;   // 32 bytes of the 128-byte step
   uint32_t sc;    // scale byte of this quarter
 };
 
@@ -75,6 +75,7 @@ constexpr int abuf_bytes() {
 
 template <int FMT, int STAGE, bool PACKED, int PF>
 __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
+  static_assert(PF >= 1 && PF <= 3, "ring depth");
   typedef typename std::conditional<FMT == 2, BFrag8, BFrag4>::type BFrag;
   typedef typename std::conditional<FMT == 2, AStage8, AStage4>::type AStage;
   constexpr int ABUF = abuf_bytes<FMT>();
@@ -118,10 +119,10 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   const uint8_t* asc = a.a_sc + (size_t)at * sc_bytes;
   auto aload = [&](int s, AStage& st) {
     if constexpr (FMT == 1) {
-      st.q = *reinterpret_cast<const uint4*>(acode + s * 64 + 16 * aq);
+      st.q = *reinterpret_cast<const v4u*>(acode + s * 64 + 16 * aq);
       st.sc = *reinterpret_cast<const uint16_t*>(asc + s * 8 + 2 * aq);
     } else {
-      const uint4* p = reinterpret_cast<const uint4*>(acode + s * 128 + 32 * aq);
+      const v4u* p = reinterpret_cast<const v4u*>(acode + s * 128 + 32 * aq);
       st.lo = p[0];
       st.hi = p[1];
       st.sc = asc[s * 4 + aq];
@@ -145,8 +146,8 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
       // 2(aq%2)+1: their first halves for aq < 2, second halves for aq >= 2
       const int h = aq >> 1, g0 = 2 * (aq & 1);
       uint8_t* T = A + f * 2112;
-      *reinterpret_cast<uint4*>(T + 1024 * h + (rr + 16 * g0) * 16) = st.lo;
-      *reinterpret_cast<uint4*>(T + 1024 * h + (rr + 16 * (g0 + 1)) * 16) = st.hi;
+      *reinterpret_cast<v4u*>(T + 1024 * h + (rr + 16 * g0) * 16) = st.lo;
+      *reinterpret_cast<v4u*>(T + 1024 * h + (rr + 16 * (g0 + 1)) * 16) = st.hi;
       T[2048 + rr + 16 * aq] = (uint8_t)st.sc;
     }
   };
@@ -175,22 +176,22 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
     for (int c = 0; c < 4; c++) {
       if constexpr (FMT == 1) {
         if (PACKED) {
-          B[c].q = *reinterpret_cast<const uint4*>(brow[c] + (size_t)s * 1024 + 16 * lane);
+          B[c].q = *reinterpret_cast<const v4u*>(brow[c] + (size_t)s * 1024 + 16 * lane);
           B[c].sc = *reinterpret_cast<const uint16_t*>(bsrow[c] + s * 128 + 2 * lane);
         } else {
-          B[c].q = *reinterpret_cast<const uint4*>(brow[c] + s * 64 + 16 * g);
+          B[c].q = *reinterpret_cast<const v4u*>(brow[c] + s * 64 + 16 * g);
           const uint8_t* sp = bsrow[c] + s * 8 + 2 * g;
           B[c].sc = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
         }
       } else {
         if (PACKED) {
           const uint8_t* t = brow[c] + (size_t)s * 2048 + 16 * lane;
-          B[c].lo = *reinterpret_cast<const uint4*>(t);
-          B[c].hi = *reinterpret_cast<const uint4*>(t + 1024);
+          B[c].lo = *reinterpret_cast<const v4u*>(t);
+          B[c].hi = *reinterpret_cast<const v4u*>(t + 1024);
           B[c].sc = bsrow[c][s * 64 + lane];
         } else {
-          B[c].lo = *reinterpret_cast<const uint4*>(brow[c] + s * 128 + 16 * g);
-          B[c].hi = *reinterpret_cast<const uint4*>(brow[c] + s * 128 + 64 + 16 * g);
+          B[c].lo = *reinterpret_cast<const v4u*>(brow[c] + s * 128 + 16 * g);
+          B[c].hi = *reinterpret_cast<const v4u*>(brow[c] + s * 128 + 64 + 16 * g);
           B[c].sc = bsrow[c][s * 4 + g];
         }
       }
@@ -238,8 +239,8 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const uint8_t* T = A + (4 * wm + i) * 2112;
-        const uint4 lo = *reinterpret_cast<const uint4*>(T + 16 * lane);
-        const uint4 hi = *reinterpret_cast<const uint4*>(T + 1024 + 16 * lane);
+        const v4u lo = *reinterpret_cast<const v4u*>(T + 16 * lane);
+        const v4u hi = *reinterpret_cast<const v4u*>(T + 1024 + 16 * lane);
         const v8i av = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         const int as = T[2048 + lane];
 #pragma unroll
@@ -264,17 +265,22 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   astore(0, ast[0]);
   aload(min(PF, NS - 1), ast[0]);
   __syncthreads();
+  // ring slots are compile-time constants (a runtime slot index would put
+  // the staging registers in scratch memory)
+  auto one_step = [&](auto J, int s0) {
+    constexpr int j = decltype(J)::value;
+    const int step = s0 + j;
+    compute(step & 1, bring[j]);
+    bload(min(step + PF, NS - 1), bring[j]);
+    // the next step's activations sit in slot (j+1)%PF; refill it after
+    astore((step + 1) & 1, ast[(j + 1) % PF]);
+    aload(min(step + 1 + PF, NS - 1), ast[(j + 1) % PF]);
+    __syncthreads();
+  };
   for (int s0 = 0; s0 < NS; s0 += PF) {
-#pragma unroll
-    for (int j = 0; j < PF; j++) {
-      const int step = s0 + j;
-      compute(step & 1, bring[j]);
-      bload(min(step + PF, NS - 1), bring[j]);
-      // the next step's activations sit in slot (j+1)%PF; refill it after
-      astore((step + 1) & 1, ast[(j + 1) % PF]);
-      aload(min(step + 1 + PF, NS - 1), ast[(j + 1) % PF]);
-      __syncthreads();
-    }
+    one_step(std::integral_constant<int, 0>{}, s0);
+    if constexpr (PF > 1) one_step(std::integral_constant<int, 1>{}, s0);
+    if constexpr (PF > 2) one_step(std::integral_constant<int, 2>{}, s0);
   }
 
   // ---- epilogue straight from registers -----------------------------------
