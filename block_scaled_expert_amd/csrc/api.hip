@@ -50,7 +50,7 @@ Layout layout(const moe_config* c, int T) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  L.z = take((size_t)T * E * 4);
+  L.z = take(router_z_rows(T) * E * 4);
   L.xq = take((size_t)T * (nv ? H / 2 : H));
   L.xs = take((size_t)T * (nv ? H / 16 : H / 32));
   L.xg = take((size_t)T * 4);

@@ -131,8 +131,11 @@ __global__ __launch_bounds__(256) void k_disp_scatter(const int32_t* __restrict_
 
 // Small batches (P <= kSmallP pairs): the whole dispatch in one 1024-thread
 // workgroup -- LDS histogram, one scan over the experts (offsets and the tile
-// list), then passes of 1024 pairs ranked against the earlier pairs of the
-// same pass and the running per-expert counts of the passes before.
+// list), then passes of 1024 pairs.  In a pass each wavefront finds, with
+// ballots over the bits of the expert id, the lanes that share a lane's
+// expert; a pair's rank is the number of such lanes below it plus the pairs
+// of that expert placed before its wavefront, which the wavefronts add to a
+// running per-expert count in wavefront order.
 constexpr int kSmallP = 4096;
 
 __global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__ ids, int P, int E_begin,
@@ -140,10 +143,9 @@ __global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__
                                                      int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
                                                      int32_t* __restrict__ worklist,
                                                      int32_t* __restrict__ ntiles) {
-  __shared__ int32_t cnt[1024], off[1024], toff[1024], run[1024], sub[1024];
-  const int i = threadIdx.x;
+  __shared__ int32_t cnt[1024], off[1024], toff[1024];
+  const int i = threadIdx.x, wave = i >> 6, lane = i & 63;
   cnt[i] = 0;
-  run[i] = 0;
   __syncthreads();
   for (int p = i; p < P; p += 1024) {
     const int e = ids[p] - E_begin;
@@ -175,8 +177,10 @@ __global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__
     }
   }
   __syncthreads();
-  off[i] = excl;                               // exclusive offsets for the scatter
+  off[i] = excl;                               // exclusive offsets
+  cnt[i] = 0;                                  // pairs placed so far, per expert
   __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
   for (int p0 = 0; p0 < P; p0 += 1024) {
     const int p = p0 + i;
     int e = -1;
@@ -184,22 +188,29 @@ __global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__
       e = ids[p] - E_begin;
       if (e < 0 || e >= E_local) e = -1;
     }
-    sub[i] = e;
-    __syncthreads();
-    int rank = 0;
-    for (int j = 0; j < i; j++) rank += sub[j] == e ? 1 : 0;
-    if (p < P) {
-      if (e >= 0) {
-        const int q = off[e] + run[e] + rank;
+    if (p < P && e < 0 && pos != nullptr) pos[p] = -1;
+    // lanes of this wavefront with the same value of e + 1 (11 bits)
+    const uint32_t v = (uint32_t)(e + 1);
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 11; b++) {
+      const uint64_t bal = __ballot((v >> b) & 1u);
+      same &= ((v >> b) & 1u) ? bal : ~bal;
+    }
+    const int rank = __popcll(same & below);
+    const int total = __popcll(same);
+    const bool last = (same & ~below & ~(1ull << lane)) == 0ull;
+    const int waves = min(16, (P - p0 + 63) / 64);   // wavefronts holding pairs
+    for (int w = 0; w < waves; w++) {
+      if (wave == w && e >= 0) {
+        const int base = cnt[e];               // read by every lane before the last lane writes
+        const int q = off[e] + base + rank;
         if (sorted != nullptr) sorted[q] = p;
         if (pos != nullptr) pos[p] = q;
-      } else if (pos != nullptr) {
-        pos[p] = -1;
+        if (last) cnt[e] = base + total;
       }
+      __syncthreads();
     }
-    __syncthreads();                           // every rank read run[] before it moves
-    if (e >= 0) atomicAdd(&run[e], 1);
-    __syncthreads();
   }
 }
 

@@ -12,6 +12,8 @@
 #include "moe_common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace moe {
 
 template <int MS, int NS>
@@ -84,8 +86,123 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   }
 }
 
-// One wave per token.  E <= 1024 (16 scores per lane), k <= 32.
-__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ z, int T, int E,
+constexpr int kMaxSplits = 6;   // largest router_splits() value
+
+// Small batches: the K range is also split over the grid's y dimension, so
+// that the 3.5 MB router weight is streamed by many CUs at once.  Workgroup
+// (expert tile x, split y, token group z) of 4 waves owns 16 experts x
+// 16*MT tokens; each wave issues all loads of its k steps before its MFMAs.
+// The partial sums zpart[y][t][e] are added in split order by the top-k
+// kernel, so the result does not depend on scheduling.
+template <int MT>
+__global__ __launch_bounds__(256) void k_router_logits_split(const uint16_t* __restrict__ x, int T, int H,
+                                                             const uint16_t* __restrict__ wr, int E, int S,
+                                                             float* __restrict__ zpart) {
+  constexpr int U = 3;                                // k steps per batch of loads
+  __shared__ float red[4][16 * MT][17];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int e0 = blockIdx.x * 16, split = blockIdx.y, t0 = blockIdx.z * 16 * MT;
+  const int nsteps = H / 64;
+  const int s_lo = split * nsteps / S, s_hi = (split + 1) * nsteps / S;
+  const int w_lo = s_lo + wave * (s_hi - s_lo) / 4, w_hi = s_lo + (wave + 1) * (s_hi - s_lo) / 4;
+
+  // rows past E or T read a valid row; their sums are never stored
+  const uint16_t* wrow = wr + (size_t)min(e0 + r, E - 1) * H + 16 * g;
+  const uint16_t* xrow[MT];
+#pragma unroll
+  for (int i = 0; i < MT; i++) xrow[i] = x + (size_t)min(t0 + 16 * i + r, T - 1) * H + 16 * g;
+
+  v4f acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; i++) acc[i] = v4f{0, 0, 0, 0};
+  const v4u zero = v4u{0, 0, 0, 0};
+  for (int s0 = w_lo; s0 < w_hi; s0 += U) {
+    v4u b[U][2], a[U][MT][2];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int k0 = min(s0 + u, w_hi - 1) * 64;
+      b[u][0] = *reinterpret_cast<const v4u*>(wrow + k0);
+      b[u][1] = *reinterpret_cast<const v4u*>(wrow + k0 + 8);
+#pragma unroll
+      for (int i = 0; i < MT; i++) {
+        a[u][i][0] = *reinterpret_cast<const v4u*>(xrow[i] + k0);
+        a[u][i][1] = *reinterpret_cast<const v4u*>(xrow[i] + k0 + 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const bool live = s0 + u < w_hi;               // a repeated step adds zero
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const v4u bv = live ? b[u][h] : zero;
+#pragma unroll
+        for (int i = 0; i < MT; i++)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[u][i][h]),
+                                                           __builtin_bit_cast(v8bf, bv), acc[i], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MT; i++)
+#pragma unroll
+    for (int q = 0; q < 4; q++) red[wave][16 * i + 4 * g + q][r] = acc[i][q];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 16 * MT * 16; idx += 256) {
+    const int m = idx >> 4, n = idx & 15;
+    const float v = ((red[0][m][n] + red[1][m][n]) + red[2][m][n]) + red[3][m][n];
+    const int t = t0 + m, e = e0 + n;
+    if (t < T && e < E) zpart[((size_t)split * T + t) * E + e] = v;
+  }
+}
+
+// Selection keys: the fp32 selection score mapped to an unsigned integer of
+// the same order, above the complement of the expert id, so that the larger
+// key is the larger score and, between equal scores, the lower expert.
+// Key 0 is below every real key.
+__device__ inline uint64_t sel_key(float v, int e) {
+  const uint32_t b = f_bits(v);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ inline float key_score(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return bits_f((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ inline int key_expert(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+
+template <int CTRL>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ inline uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Maximum over the wavefront: inside each row of 16 lanes with DPP (swap
+// neighbours, swap pairs, mirror the half rows, mirror the row), then over the
+// four rows.  The result is wave-uniform.
+__device__ inline uint64_t wave_max_key(uint64_t k) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(k);  k = o > k ? o : k;    // quad_perm [1,0,3,2]
+  o = dpp_u64<0x4E>(k);  k = o > k ? o : k;    // quad_perm [2,3,0,1]
+  o = dpp_u64<0x141>(k); k = o > k ? o : k;    // row_half_mirror
+  o = dpp_u64<0x140>(k); k = o > k ? o : k;    // row_mirror
+  const uint64_t r0 = readlane_u64(k, 0), r1 = readlane_u64(k, 16);
+  const uint64_t r2 = readlane_u64(k, 32), r3 = readlane_u64(k, 48);
+  const uint64_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
+}
+
+// One wave per token; lane l holds experts l + 64 i.  Logits are the sum of
+// S split partials (S = 1: the plain logits), added in split order.  k + 1
+// rounds of a wavefront arg-max give the top-k and the (k+1)-th score for
+// the near-tie flag.  E <= 64 * NPER, k <= 32.
+template <int NPER>
+__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ zpart, int S, int T, int E,
                                                      const float* __restrict__ bias, int k,
                                                      int norm_topk, float routed_scale,
                                                      int32_t* __restrict__ ids,
@@ -94,89 +211,104 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ z
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  constexpr int kMaxPer = 16;
-  float sc[kMaxPer], sel[kMaxPer];
-  const float* zt = z + (size_t)t * E;
+  float sc[NPER];
+  uint64_t key[NPER];
+  // every load in one batch (clamped addresses, no branches); splits past S
+  // add +0, which leaves the sum unchanged
+  const size_t split_stride = (size_t)T * E;
+  float zz[NPER][kMaxSplits], bb[NPER];
 #pragma unroll
-  for (int i = 0; i < kMaxPer; i++) {
+  for (int i = 0; i < NPER; i++) {
+    const int ec = min(lane + 64 * i, E - 1);
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; sp++) zz[i][sp] = zpart[min(sp, S - 1) * split_stride + (size_t)t * E + ec];
+    bb[i] = bias[ec];
+  }
+#pragma unroll
+  for (int i = 0; i < NPER; i++) {
     const int e = lane + 64 * i;
-    if (e < E) {
-      sc[i] = 1.0f / (1.0f + expf(-zt[e]));
-      sel[i] = sc[i] + bias[e];
-    } else {
-      sc[i] = 0.0f;
-      sel[i] = -INFINITY;
-    }
+    float z = zz[i][0];
+#pragma unroll
+    for (int sp = 1; sp < kMaxSplits; sp++) z += sp < S ? zz[i][sp] : 0.0f;
+    sc[i] = 1.0f / (1.0f + expf(-z));
+    key[i] = e < E ? sel_key(sc[i] + bb[i], e) : 0ull;
   }
   float chosen_s = 0.0f;   // lane j < k keeps the score of the j-th choice
   int chosen_id = 0;
-  float kth = 0.0f, next = -INFINITY;
+  float tot = 0.0f, kth = 0.0f, next = -INFINITY;
   const int rounds = k < E ? k + 1 : k;
   for (int j = 0; j < rounds; j++) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    uint64_t m = key[0];
 #pragma unroll
-    for (int i = 0; i < kMaxPer; i++) {
-      const int e = lane + 64 * i;
-      if (e < E && (sel[i] > bv || (sel[i] == bv && e < bi))) {
-        bv = sel[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    for (int i = 1; i < NPER; i++) m = key[i] > m ? key[i] : m;
+    const uint64_t best = wave_max_key(m);
     if (j == k) {
-      next = bv;
+      next = key_score(best);
       break;
     }
-    if (j == k - 1) kth = bv;
-    const int owner = bi & 63, slot = bi >> 6;
-    float s_of = 0.0f;
-    if (lane == owner) {
+    const int be = key_expert(best);
+    if (j == k - 1) kth = key_score(best);
+    const int owner = be & 63, slot = be >> 6;
+    float v = 0.0f;
 #pragma unroll
-      for (int i = 0; i < kMaxPer; i++)
-        if (i == slot) {
-          s_of = sc[i];
-          sel[i] = -INFINITY;
-        }
+    for (int i = 0; i < NPER; i++) {
+      v = i == slot ? sc[i] : v;
+      if (lane == owner && i == slot) key[i] = 0ull;
     }
-    s_of = __shfl(s_of, owner, kWave);
+    const float s_of = bits_f(__builtin_amdgcn_readlane((int)f_bits(v), owner));
+    tot += s_of;                                      // gate-weight sum in j order
     if (lane == j) {
       chosen_s = s_of;
-      chosen_id = bi;
+      chosen_id = be;
     }
   }
-  // gate weights: sum in j order
-  float tot = 0.0f;
-  for (int j = 0; j < k; j++) tot += __shfl(chosen_s, j, kWave);
   if (lane < k) {
-    float wj = norm_topk ? chosen_s / tot : chosen_s;
+    const float wj = norm_topk ? chosen_s / tot : chosen_s;
     ids[(size_t)t * k + lane] = chosen_id;
     w[(size_t)t * k + lane] = wj * routed_scale;
   }
   if (lane == 0 && near_tie != nullptr) near_tie[t] = (k < E && (kth - next) < 1e-6f) ? 1 : 0;
 }
 
+int router_splits(int T) { return T <= 64 ? 6 : T <= 128 ? 4 : T <= 256 ? 2 : 1; }
+
+size_t router_z_rows(int max_tokens) {
+  size_t r = (size_t)max_tokens;
+  const int caps[3] = {64, 128, 256};
+  for (int c : caps) {
+    const int t = min(max_tokens, c);
+    r = std::max(r, (size_t)t * router_splits(t));
+  }
+  return r;
+}
+
 int launch_router(const uint16_t* x, int T, int H, const uint16_t* wr, const float* bias, int E,
                   int k, int norm_topk, float routed_scale, float* z, int32_t* ids, float* w,
                   uint8_t* near_tie, hipStream_t stream) {
   if (T <= 0) return 0;
-  if (T >= 2048) {
+  const int S = router_splits(T);
+  if (S > 1) {
+    const int mt = T <= 16 ? 1 : T <= 32 ? 2 : 4;
+    const dim3 grid(ceil_div(E, 16), S, ceil_div(T, 16 * mt));
+    if (mt == 1) hipLaunchKernelGGL((k_router_logits_split<1>), grid, dim3(256), 0, stream, x, T, H, wr, E, S, z);
+    else if (mt == 2) hipLaunchKernelGGL((k_router_logits_split<2>), grid, dim3(256), 0, stream, x, T, H, wr, E, S, z);
+    else hipLaunchKernelGGL((k_router_logits_split<4>), grid, dim3(256), 0, stream, x, T, H, wr, E, S, z);
+  } else if (T >= 2048) {
     const dim3 grid(ceil_div(T, 64), ceil_div(E, 64));
     hipLaunchKernelGGL((k_router_logits<4, 4>), grid, dim3(256), 0, stream, x, T, H, wr, E, z);
   } else {
     const dim3 grid(ceil_div(T, 16), ceil_div(E, 16));
     hipLaunchKernelGGL((k_router_logits<1, 1>), grid, dim3(256), 0, stream, x, T, H, wr, E, z);
   }
-  hipLaunchKernelGGL(k_router_topk, dim3(ceil_div(T, 4)), dim3(256), 0, stream, z, T, E, bias, k,
-                     norm_topk, routed_scale, ids, w, near_tie);
+  const dim3 tg(ceil_div(T, 4));
+#define MOE_TOPK(N) \
+  hipLaunchKernelGGL(k_router_topk<N>, tg, dim3(256), 0, stream, z, S, T, E, bias, k, norm_topk, routed_scale, ids, w, near_tie)
+  if (E <= 64) MOE_TOPK(1);
+  else if (E <= 128) MOE_TOPK(2);
+  else if (E <= 256) MOE_TOPK(4);
+  else if (E <= 512) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
