@@ -72,6 +72,14 @@ def upload_weights(w, bse_cfg):
     return dev, per_expert
 
 
+def gemm_source(workload: str) -> str:
+    """Source file of the expert GEMM kernel a workload runs: decode batches
+    (a few rows per expert) take k_expert_gemm, prefill chunks and
+    expert-parallel shares (128-row tiles) take k_expert_gemm_big."""
+    small = workload.startswith("decode") or workload == "tiny"
+    return "gemm.hip" if small else "gemm_big.hip"
+
+
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes (fetch + write) per launch of `kernel` ("gate_up" / "down")
     recorded from rocprofv3 counters in profiles/traffic.json, if the GEMM
@@ -81,8 +89,10 @@ def measured_traffic(workload: str, kernel: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(workload)
-    src = open(os.path.join(ROOT, "block_scaled_expert_amd", "csrc", "gemm.hip"), "rb").read()
-    if not rec or rec.get("gemm_hip_sha256") != hashlib.sha256(src).hexdigest() or kernel not in rec:
+    fname = gemm_source(workload)
+    src = open(os.path.join(ROOT, "block_scaled_expert_amd", "csrc", fname), "rb").read()
+    if (not rec or rec.get("source_file") != fname or rec.get("source_sha256") != hashlib.sha256(src).hexdigest()
+            or kernel not in rec):
         return None
     return rec[kernel]["fetch_bytes"] + rec[kernel]["write_bytes"]
 
@@ -236,20 +246,21 @@ def main() -> int:
     alg_bytes = expert_bytes + E * H * 2 + E * 4 + 2 * T * H * 2
 
     decode = w.key.startswith("decode") or w.key == "tiny"
+    gemm_kernel = "k_expert_gemm" if gemm_source(w.key) == "gemm.hip" else "k_expert_gemm_big"
     if decode or w.key.startswith("ep8"):
         achieved = active * w13_bytes / (stage_ms["gate_up"] * 1e-3) / 1e9
         tr = measured_traffic(w.key, "gate_up") if args.layout == "packed" else None
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
                 "traffic_over_algorithmic": None if tr is None else round(tr / (active * w13_bytes), 4),
-                "kernel": "k_expert_gemm gate/up", "per_launch": f"{active} experts x {w13_bytes} B (w13 codes + scales)"}
+                "kernel": gemm_kernel + " gate/up", "per_launch": f"{active} experts x {w13_bytes} B (w13 codes + scales)"}
     else:
         issued = MFMA_ISSUED[w.fmt]
         achieved = flops_gu / (stage_ms["gate_up"] * 1e-3) / 1e12
         tr = measured_traffic(w.key, "gate_up") if args.layout == "packed" else None
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS[issued], "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_PEAK_TFLOPS[issued], 4), "traffic": tr,
-                "kernel": "k_expert_gemm gate/up", "mfma_issued": issued,
+                "kernel": gemm_kernel + " gate/up", "mfma_issued": issued,
                 "frac_of_fp8_peak": round(achieved / MFMA_PEAK_TFLOPS["fp8"], 4),
                 "frac_of_fp4_peak": round(achieved / MFMA_PEAK_TFLOPS["fp4"], 4),
                 "per_launch": f"2 x {local_pairs} pairs x {2 * w.ffn} x {H} flop"}
