@@ -81,6 +81,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   constexpr int ABUF = abuf_bytes<FMT>();
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int tok[BM];
+  __shared__ float rgs[BM];
 
   // XCD-aware order: work item L = (weight tile L / nt, row tile L % nt);
   // consecutive items of one XCD are consecutive row tiles of one weight tile
@@ -106,7 +107,13 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   const uint8_t* wexp = a.w_codes + (size_t)el * NW * row_bytes;
   const uint8_t* wsexp = a.w_sc + (size_t)el * NW * sc_bytes;
 
-  if (tid < BM) tok[tid] = tid < rows ? (STAGE == 0 ? a.sorted[row0 + tid] / a.k : row0 + tid) : -1;
+  // token of each row and (NVFP4) its activation row scale, read once here:
+  // a load under the epilogue's row test would wait for memory once per row
+  if (tid < BM) {
+    const int tk = tid < rows ? (STAGE == 0 ? a.sorted[row0 + tid] / a.k : row0 + tid) : -1;
+    tok[tid] = tk;
+    if (FMT == 1) rgs[tid] = tk >= 0 ? a.a_gs[tk] : 0.0f;
+  }
   __syncthreads();
 
   // ---- activation staging ------------------------------------------------
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
       for (int q = 0; q < 4; q++) {
         const int m = 64 * wm + 16 * i + 4 * g4 + q;
         if (m >= rows) continue;
-        const float ga = FMT == 1 ? a.a_gs[tok[m]] : 1.0f;
+        const float ga = FMT == 1 ? rgs[m] : 1.0f;
 #pragma unroll
         for (int c = 0; c < 2; c++) {
           float gv = acc[i][c][q], uv = acc[i][c + 2][q];
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
       for (int q = 0; q < 4; q++) {
         const int m = 64 * wm + 16 * i + 4 * g4 + q;
         if (m >= rows) continue;
-        const float ha = FMT == 1 ? a.a_gs[row0 + m] : 1.0f;
+        const float ha = FMT == 1 ? rgs[m] : 1.0f;
 #pragma unroll
         for (int c = 0; c < 4; c++) {
           float yv = acc[i][c][q];
