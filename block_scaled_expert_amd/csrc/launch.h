@@ -14,10 +14,10 @@ namespace moe {
 int launch_quant(int fmt, int dtype, const void* x, int rows, const int* rows_dev, int cols,
                  uint8_t* codes, uint8_t* scales, float* gs, hipStream_t stream);
 
-// Router: logits into z (fp32 workspace: router_splits(T) partial [T][E]
+// Router: logits into z (fp32 workspace: router_splits(T, E) partial [T][E]
 // planes, router_z_rows(max_tokens) * E floats at most), then sigmoid + bias
 // + top-k.
-int router_splits(int T);
+int router_splits(int T, int E);
 size_t router_z_rows(int max_tokens);
 int launch_router(const uint16_t* x, int T, int H, const uint16_t* wr, const float* bias, int E,
                   int k, int norm_topk, float routed_scale, float* z, int32_t* ids, float* w,

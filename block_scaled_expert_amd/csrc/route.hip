@@ -4,87 +4,17 @@
 // the router's sigmoid, bias and top-k are one fused step; Miles docs
 // section 1: sigmoid routing, 384 experts, top-8).
 //
-// Logits: a workgroup of 4 waves owns a (16*MS tokens) x (16*NS experts)
-// tile; the waves split K four ways and their partial tiles are summed in a
-// fixed order through LDS.  MFMA 16x16x32 bf16: lane l holds row l%16 and
-// k-group l/16 of 8 elements; each lane loads 16 consecutive bf16 (32 bytes)
-// and feeds them to two MFMAs, the B operand using the same k mapping.
+// Logits are computed as S partial sums over slices of K (S = 1..6) written
+// to S planes; the top-k kernel adds them in slice order, so the result does
+// not depend on scheduling.  MFMA 16x16x32 bf16: lane l holds row l%16 and
+// k-group l/16 of 8 elements; each lane feeds 16 consecutive bf16 (32 bytes)
+// to two MFMAs, the B operand using the same k mapping.
 #include "moe_common.h"
 #include "launch.h"
 
 #include <algorithm>
 
 namespace moe {
-
-template <int MS, int NS>
-__global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x, int T, int H,
-                                                       const uint16_t* __restrict__ wr, int E,
-                                                       float* __restrict__ z) {
-  __shared__ float red[4][16 * MS][16 * NS + 1];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * 16 * MS, e0 = blockIdx.y * 16 * NS;
-  const int r = lane & 15, g = lane >> 4;
-  const int nsteps = H / 64;                        // 64 k per step (two MFMAs)
-  const int s_begin = wave * nsteps / 4, s_end = (wave + 1) * nsteps / 4;
-
-  v4f acc[MS][NS];
-#pragma unroll
-  for (int i = 0; i < MS; i++)
-#pragma unroll
-    for (int j = 0; j < NS; j++) acc[i][j] = v4f{0, 0, 0, 0};
-
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  for (int s = s_begin; s < s_end; s++) {
-    const int k0 = s * 64 + 16 * g;
-    uint4 a[MS][2], b[NS][2];
-#pragma unroll
-    for (int i = 0; i < MS; i++) {
-      const int t = t0 + 16 * i + r;
-      if (t < T) {
-        const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * H + k0);
-        a[i][0] = p[0];
-        a[i][1] = p[1];
-      } else {
-        a[i][0] = zero4;
-        a[i][1] = zero4;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NS; j++) {
-      const int e = e0 + 16 * j + r;
-      if (e < E) {
-        const uint4* p = reinterpret_cast<const uint4*>(wr + (size_t)e * H + k0);
-        b[j][0] = p[0];
-        b[j][1] = p[1];
-      } else {
-        b[j][0] = zero4;
-        b[j][1] = zero4;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < 2; h++)
-#pragma unroll
-      for (int i = 0; i < MS; i++)
-#pragma unroll
-        for (int j = 0; j < NS; j++)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(v8bf, a[i][h]), __builtin_bit_cast(v8bf, b[j][h]), acc[i][j], 0, 0, 0);
-  }
-  // output layout: acc reg q of lane l is D[4*(l/16)+q][l%16]
-#pragma unroll
-  for (int i = 0; i < MS; i++)
-#pragma unroll
-    for (int j = 0; j < NS; j++)
-#pragma unroll
-      for (int q = 0; q < 4; q++) red[wave][16 * i + 4 * g + q][16 * j + r] = acc[i][j][q];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 16 * MS * 16 * NS; idx += 256) {
-    const int m = idx / (16 * NS), n = idx % (16 * NS);
-    const float v = ((red[0][m][n] + red[1][m][n]) + red[2][m][n]) + red[3][m][n];
-    const int t = t0 + m, e = e0 + n;
-    if (t < T && e < E) z[(size_t)t * E + e] = v;
-  }
-}
 
 constexpr int kMaxSplits = 6;   // largest router_splits() value
 
@@ -154,6 +84,100 @@ __global__ __launch_bounds__(256) void k_router_logits_split(const uint16_t* __r
     const int t = t0 + m, e = e0 + n;
     if (t < T && e < E) zpart[((size_t)split * T + t) * E + e] = v;
   }
+}
+
+// Larger batches: a workgroup of 4 waves (2 x 2) computes a 128-token x
+// 128-expert tile over one K slice (grid z = split).  Each 64-wide k step of
+// both operands is staged in LDS in MFMA lane order (chunk q of 16 bytes at
+// byte 16 q: row tile q/128, k half (q/64)%2, lane q%64), so every wavefront
+// store and load is 1 KB contiguous; the next step is fetched into registers
+// while the current one is multiplied.  Each wave owns 64 x 64 outputs over
+// the whole slice and writes its partial plane directly.
+__global__ __launch_bounds__(256) void k_router_logits_tiled(const uint16_t* __restrict__ x, int T, int H,
+                                                             const uint16_t* __restrict__ wr, int E, int S,
+                                                             float* __restrict__ zpart) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][16384];   // [buffer][A, B][8 tiles x 2 halves x 64 lanes x 16 B]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int t0 = blockIdx.x * 128, e0 = blockIdx.y * 128, split = blockIdx.z;
+  const int nsteps = H / 64;
+  const int s_lo = split * nsteps / S, s_hi = (split + 1) * nsteps / S;
+
+  // staging: thread takes chunks q = tid + 256 u (u < 4) of each operand;
+  // rows past T / E read a valid row (their sums are never stored)
+  const uint16_t* ap[4];
+  const uint16_t* bp[4];
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int q = tid + 256 * u, f = q >> 7, hh = (q >> 6) & 1, l = q & 63;
+    const int koff = 32 * hh + 8 * (l >> 4);
+    ap[u] = x + (size_t)min(t0 + 16 * f + (l & 15), T - 1) * H + koff;
+    bp[u] = wr + (size_t)min(e0 + 16 * f + (l & 15), E - 1) * H + koff;
+  }
+  v4u sa[4], sb[4];
+  auto gload = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      sa[u] = *reinterpret_cast<const v4u*>(ap[u] + st * 64);
+      sb[u] = *reinterpret_cast<const v4u*>(bp[u] + st * 64);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      *reinterpret_cast<v4u*>(&lds[buf][0][16 * (tid + 256 * u)]) = sa[u];
+      *reinterpret_cast<v4u*>(&lds[buf][1][16 * (tid + 256 * u)]) = sb[u];
+    }
+  };
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = v4f{0, 0, 0, 0};
+
+  if (s_hi > s_lo) {
+    gload(s_lo);
+    lstore(0);
+    gload(min(s_lo + 1, s_hi - 1));
+    __syncthreads();
+    for (int st = s_lo; st < s_hi; st++) {
+      const int buf = (st - s_lo) & 1;
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        v4u av[4], bv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          av[i] = *reinterpret_cast<const v4u*>(&lds[buf][0][16 * ((4 * wm + i) * 128 + hh * 64 + lane)]);
+          bv[i] = *reinterpret_cast<const v4u*>(&lds[buf][1][16 * ((4 * wn + i) * 128 + hh * 64 + lane)]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[i]),
+                                                                __builtin_bit_cast(v8bf, bv[j]), acc[i][j], 0, 0, 0);
+      }
+      lstore(buf ^ 1);                        // the buffer read one step ago
+      gload(min(st + 2, s_hi - 1));
+      __syncthreads();
+    }
+  }
+  // acc reg q of lane l in tile (i, j): token row 16 i + 4 (l/16) + q of the
+  // wave's 64, expert column 16 j + l%16
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int t = t0 + 64 * wm + 16 * i + 4 * g + q;
+      if (t >= T) continue;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int e = e0 + 64 * wn + 16 * j + r;
+        if (e < E) zpart[((size_t)split * T + t) * E + e] = acc[i][j][q];
+      }
+    }
 }
 
 // Selection keys: the fp32 selection score mapped to an unsigned integer of
@@ -270,35 +294,30 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ z
   if (lane == 0 && near_tie != nullptr) near_tie[t] = (k < E && (kth - next) < 1e-6f) ? 1 : 0;
 }
 
-int router_splits(int T) { return T <= 64 ? 6 : T <= 128 ? 4 : T <= 256 ? 2 : 1; }
-
-size_t router_z_rows(int max_tokens) {
-  size_t r = (size_t)max_tokens;
-  const int caps[3] = {64, 128, 256};
-  for (int c : caps) {
-    const int t = min(max_tokens, c);
-    r = std::max(r, (size_t)t * router_splits(t));
-  }
-  return r;
+// K splits: small batches (split-K GEMV, 6 / 4 / 2 planes); larger ones
+// (128 x 128 tiles) take enough splits for about 512 workgroups, at most 6.
+int router_splits(int T, int E) {
+  if (T <= 256) return T <= 64 ? 6 : T <= 128 ? 4 : 2;
+  const int tiles = ceil_div(T, 128) * ceil_div(E, 128);
+  return std::min(kMaxSplits, std::max(1, ceil_div(512, tiles)));
 }
+
+size_t router_z_rows(int max_tokens) { return (size_t)kMaxSplits * (size_t)std::max(max_tokens, 0); }
 
 int launch_router(const uint16_t* x, int T, int H, const uint16_t* wr, const float* bias, int E,
                   int k, int norm_topk, float routed_scale, float* z, int32_t* ids, float* w,
                   uint8_t* near_tie, hipStream_t stream) {
   if (T <= 0) return 0;
-  const int S = router_splits(T);
-  if (S > 1) {
+  const int S = router_splits(T, E);
+  if (T <= 256) {
     const int mt = T <= 16 ? 1 : T <= 32 ? 2 : 4;
     const dim3 grid(ceil_div(E, 16), S, ceil_div(T, 16 * mt));
     if (mt == 1) hipLaunchKernelGGL((k_router_logits_split<1>), grid, dim3(256), 0, stream, x, T, H, wr, E, S, z);
     else if (mt == 2) hipLaunchKernelGGL((k_router_logits_split<2>), grid, dim3(256), 0, stream, x, T, H, wr, E, S, z);
     else hipLaunchKernelGGL((k_router_logits_split<4>), grid, dim3(256), 0, stream, x, T, H, wr, E, S, z);
-  } else if (T >= 2048) {
-    const dim3 grid(ceil_div(T, 64), ceil_div(E, 64));
-    hipLaunchKernelGGL((k_router_logits<4, 4>), grid, dim3(256), 0, stream, x, T, H, wr, E, z);
   } else {
-    const dim3 grid(ceil_div(T, 16), ceil_div(E, 16));
-    hipLaunchKernelGGL((k_router_logits<1, 1>), grid, dim3(256), 0, stream, x, T, H, wr, E, z);
+    const dim3 grid(ceil_div(T, 128), ceil_div(E, 128), S);
+    hipLaunchKernelGGL(k_router_logits_tiled, grid, dim3(256), 0, stream, x, T, H, wr, E, S, z);
   }
   const dim3 tg(ceil_div(T, 4));
 #define MOE_TOPK(N) \
