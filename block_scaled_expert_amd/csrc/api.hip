@@ -282,14 +282,19 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   g.cap_form = c->cap_form;
   g.cap = c->cap_form == MOE_CAP_NONE ? 1.0f : c->cap;
   g.out = at<float>(ws, L.h);
+  const bool fuse_h = c->fmt == MOE_FMT_MXFP8;   // MXFP8 h is encoded by the gate/up epilogue
+  g.out_q = fuse_h ? at<uint8_t>(ws, L.hq) : nullptr;
+  g.out_s = fuse_h ? at<uint8_t>(ws, L.hs) : nullptr;
   record(events, 2 * MOE_STAGE_GATE_UP, s);
   bad |= launch_gemm_gateup(g, s);
   record(events, 2 * MOE_STAGE_GATE_UP + 1, s);
 
-  // 4. quantize h per (token, expert) row; the row count lives on the device
+  // 4. quantize h per (token, expert) row (NVFP4: the row scale needs the
+  // whole row, so a kernel of its own; the row count lives on the device)
   record(events, 2 * MOE_STAGE_QUANT_H, s);
-  bad |= launch_quant(c->fmt, 1, at<float>(ws, L.h), P, b.offsets + EL, F, at<uint8_t>(ws, L.hq),
-                      at<uint8_t>(ws, L.hs), at<float>(ws, L.hg), s);
+  if (!fuse_h)
+    bad |= launch_quant(c->fmt, 1, at<float>(ws, L.h), P, b.offsets + EL, F, at<uint8_t>(ws, L.hq),
+                        at<uint8_t>(ws, L.hs), at<float>(ws, L.hg), s);
   record(events, 2 * MOE_STAGE_QUANT_H + 1, s);
 
   // 5. down GEMM -> y (fp32, sorted rows)

@@ -11,8 +11,9 @@
 //   offsets one workgroup: exclusive scan of totals over experts; the GEMM
 //           tile list (local expert, first row) with tile_m rows per tile
 //   scatter one workgroup per chunk: each pair's rank among the earlier
-//           pairs of its expert inside the chunk, counted explicitly, gives
-//           its sorted position; integer atomics only accumulate counts.
+//           pairs of its expert inside the chunk (ballots within a
+//           wavefront, running counts across wavefronts) gives its sorted
+//           position; integer atomics only accumulate counts.
 #include "moe_common.h"
 #include "launch.h"
 
@@ -92,6 +93,23 @@ __global__ __launch_bounds__(1024) void k_disp_offsets(const int32_t* __restrict
   }
 }
 
+// Lanes of the calling wavefront whose value of v (11 bits) equals this
+// lane's: one ballot per bit.
+__device__ inline uint64_t same_value_lanes(uint32_t v) {
+  uint64_t same = ~0ull;
+#pragma unroll
+  for (int b = 0; b < 11; b++) {
+    const uint64_t bal = __ballot((v >> b) & 1u);
+    same &= ((v >> b) & 1u) ? bal : ~bal;
+  }
+  return same;
+}
+
+// One workgroup per chunk, passes of 256 pairs.  A pair's sorted position is
+// its expert's offset + the pairs of that expert in earlier chunks (the
+// scan) + those placed by earlier passes and wavefronts of this chunk (run[],
+// advanced wavefront by wavefront) + its rank among the lanes of its
+// wavefront with the same expert (ballots).
 __global__ __launch_bounds__(256) void k_disp_scatter(const int32_t* __restrict__ ids, int P, int chunk,
                                                       int E_begin, int E_local,
                                                       const int32_t* __restrict__ counts,
@@ -99,33 +117,35 @@ __global__ __launch_bounds__(256) void k_disp_scatter(const int32_t* __restrict_
                                                       int32_t* __restrict__ sorted,
                                                       int32_t* __restrict__ pos) {
   extern __shared__ int32_t run[];            // [E_local] pairs already placed in this chunk
-  __shared__ int32_t sub[kSub];
-  for (int e = threadIdx.x; e < E_local; e += 256) run[e] = 0;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < E_local; e += 256) run[e] = 0;
+  __syncthreads();
   const int c = blockIdx.x;
   const int begin = c * chunk, end = min(P, (c + 1) * chunk);
+  const uint64_t below = (1ull << lane) - 1ull;
   for (int p0 = begin; p0 < end; p0 += kSub) {
-    const int p = p0 + threadIdx.x;
+    const int p = p0 + tid;
     int e = -1;
     if (p < end) {
       e = ids[p] - E_begin;
       if (e < 0 || e >= E_local) e = -1;
     }
-    __syncthreads();                           // previous pass done with sub / run
-    sub[threadIdx.x] = e;
-    __syncthreads();
-    int rank = 0;
-    for (int j = 0; j < kSub; j++) rank += (j < (int)threadIdx.x && sub[j] == e) ? 1 : 0;
-    if (p < end) {
-      if (e >= 0) {
-        const int q = offsets[e] + counts[(size_t)c * E_local + e] + run[e] + rank;
+    if (p < end && e < 0 && pos != nullptr) pos[p] = -1;
+    const uint64_t same = same_value_lanes((uint32_t)(e + 1));
+    const int rank = __popcll(same & below);
+    const int total = __popcll(same);
+    const bool last = (same & ~below & ~(1ull << lane)) == 0ull;
+    const int waves = min(kSub / 64, (end - p0 + 63) / 64);
+    for (int w = 0; w < waves; w++) {
+      if (wave == w && e >= 0) {
+        const int base = run[e];               // read by every lane before the last lane writes
+        const int q = offsets[e] + counts[(size_t)c * E_local + e] + base + rank;
         if (sorted != nullptr) sorted[q] = p;
         if (pos != nullptr) pos[p] = q;
-      } else if (pos != nullptr) {
-        pos[p] = -1;
+        if (last) run[e] = base + total;
       }
+      __syncthreads();
     }
-    __syncthreads();                           // all ranks read run[] before it moves
-    if (e >= 0) atomicAdd(&run[e], 1);
   }
 }
 
@@ -189,14 +209,7 @@ __global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__
       if (e < 0 || e >= E_local) e = -1;
     }
     if (p < P && e < 0 && pos != nullptr) pos[p] = -1;
-    // lanes of this wavefront with the same value of e + 1 (11 bits)
-    const uint32_t v = (uint32_t)(e + 1);
-    uint64_t same = ~0ull;
-#pragma unroll
-    for (int b = 0; b < 11; b++) {
-      const uint64_t bal = __ballot((v >> b) & 1u);
-      same &= ((v >> b) & 1u) ? bal : ~bal;
-    }
+    const uint64_t same = same_value_lanes((uint32_t)(e + 1));
     const int rank = __popcll(same & below);
     const int total = __popcll(same);
     const bool last = (same & ~below & ~(1ull << lane)) == 0ull;

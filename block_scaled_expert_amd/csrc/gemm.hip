@@ -20,9 +20,9 @@
 //   the natural memory order that is two 16-byte loads at k0 + 16g and
 //   k0 + 64 + 16g and the scale of block k0/32 + g.
 // NVFP4 (W4A4): NVFP4's E4M3 scale per 16 cannot ride the E8M0-per-32 scale
-//   operand, and E2M1 times an E4M3 scale needs up to 7 significant bits, so
+//   operand, and E2M1 times an E4M3 scale needs up to 6 significant bits, so
 //   both operands are expanded in registers to f16 = E2M1 value * block
-//   scale (exact: at most 7 bits, magnitudes 2^-10 .. 2688) and multiplied
+//   scale (exact: at most 6 bits, magnitudes 2^-10 .. 2688) and multiplied
 //   on v_mfma_f32_16x16x32_f16 (products exact in the fp32 accumulator).
 //   The two fp32 tensor/row scales are applied in the epilogue.  Each lane
 //   loads 16 bytes = 32 consecutive E2M1 codes per 128-wide k step and feeds
@@ -37,7 +37,7 @@ namespace moe {
 // E2M1 x 8 (one 32-bit word, low nibble first) -> f16 x 8, each times its
 // block scale.  The convert applies the power of two 2^8 (its scale operand
 // only contributes an exponent); the block scale enters as sigma * 2^-8 in
-// f16 (see sig_pair), so every product is exactly E2M1 * sigma: at most 7
+// f16 (see sig_pair), so every product is exactly E2M1 * sigma: at most 6
 // significant bits, magnitudes 2^-10 .. 2688, all normal f16 numbers.
 __device__ inline v8h dequant8(uint32_t word, v2h sig2) {
   const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 256.0f, 0) * sig2;
@@ -168,6 +168,7 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
   typedef typename std::conditional<FMT == 2, Frag8, Frag4>::type Frag;
   __shared__ float red[KS][TM][BN + 1];
   __shared__ int tok[TM];
+  __shared__ float rgs[TM];   // NVFP4 activation row scales (read once, not per output)
 
   const int tile = blockIdx.y;
   if (tile >= a.ntiles[0]) return;
@@ -208,7 +209,9 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
 
   if (threadIdx.x < TM) {
     const int m = threadIdx.x;
-    tok[m] = m < rows ? (STAGE == 0 ? a.sorted[row0 + m] / a.k : row0 + m) : -1;
+    const int tk = m < rows ? (STAGE == 0 ? a.sorted[row0 + m] / a.k : row0 + m) : -1;
+    tok[m] = tk;
+    if (FMT == 1) rgs[m] = tk >= 0 ? a.a_gs[tk] : 0.0f;
   }
   __syncthreads();
 
@@ -286,25 +289,41 @@ __global__ __launch_bounds__(256) void k_expert_gemm(GemmArgs a) {
     return v;
   };
   if (STAGE == 0) {
+    // 32 consecutive threads hold one row's 32 h columns; for MXFP8 they are
+    // one scale block, encoded here (amax over the 32 lanes, then each lane
+    // its code).  Every thread runs every iteration (TM * 32 is a multiple of
+    // 256), so the lane exchanges always see all 32 lanes.
     const float inv_c = 1.0f / a.cap;
     for (int idx = threadIdx.x; idx < TM * 32; idx += 256) {
       const int m = idx >> 5, c = idx & 31;
-      if (m >= rows) continue;
+      const bool live = m < rows;
       float gv = ksum(m, c), uv = ksum(m, 32 + c);
       if (FMT == 1) {
-        const float ga = a.a_gs[tok[m]];
+        const float ga = rgs[m];
         gv = (gv * ga) * a.w_gs[3 * el + 0];
         uv = (uv * ga) * a.w_gs[3 * el + 1];
       }
       const float h = cap_swiglu(gv, uv, a.cap_form, a.cap, inv_c);
-      a.out[(size_t)(row0 + m) * a.F + blockIdx.x * 32 + c] = h;
+      if (FMT == 2) {
+        float am = live ? fabsf(h) : 0.0f;
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, kWave));
+        const int E = mx_exponent(am);
+        const uint32_t code = mx_encode(h, pow2f(-E));
+        if (live) {
+          a.out_q[(size_t)(row0 + m) * a.F + blockIdx.x * 32 + c] = (uint8_t)code;
+          if (c == 0) a.out_s[(size_t)(row0 + m) * (a.F / 32) + blockIdx.x] = (uint8_t)(E + 127);
+        }
+      } else if (live) {
+        a.out[(size_t)(row0 + m) * a.F + blockIdx.x * 32 + c] = h;
+      }
     }
   } else {
     for (int idx = threadIdx.x; idx < TM * BN; idx += 256) {
       const int m = idx >> 6, c = idx & 63;
       if (m >= rows) continue;
       float yv = ksum(m, c);
-      if (FMT == 1) yv = (yv * a.a_gs[row0 + m]) * a.w_gs[3 * el + 2];
+      if (FMT == 1) yv = (yv * rgs[m]) * a.w_gs[3 * el + 2];
       a.out[(size_t)(row0 + m) * a.H + blockIdx.x * BN + c] = yv;
     }
   }

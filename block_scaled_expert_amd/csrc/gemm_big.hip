@@ -303,8 +303,9 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 64 * wm + 16 * i + 4 * g4 + q;
-        if (m >= rows) continue;
+        const bool live = m < rows;
         const float ga = FMT == 1 ? rgs[m] : 1.0f;
+        float h[2];
 #pragma unroll
         for (int c = 0; c < 2; c++) {
           float gv = acc[i][c][q], uv = acc[i][c + 2][q];
@@ -312,8 +313,27 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
             gv = (gv * ga) * wg;
             uv = (uv * ga) * wu;
           }
-          const int col = bx * 128 + 32 * wn + 16 * c + cl;
-          a.out[(size_t)(row0 + m) * a.F + col] = cap_swiglu(gv, uv, a.cap_form, a.cap, inv_c);
+          h[c] = cap_swiglu(gv, uv, a.cap_form, a.cap, inv_c);
+        }
+        const int col0 = bx * 128 + 32 * wn;
+        if (FMT == 2) {
+          // the wave's 32 columns of row m (16 lanes x 2 groups) are one MX
+          // block: amax across the 16 lanes of this row, then each lane
+          // encodes its two values; all lanes take part in the exchange
+          float am = live ? fmaxf(fabsf(h[0]), fabsf(h[1])) : 0.0f;
+#pragma unroll
+          for (int o = 8; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, kWave));
+          const int E = mx_exponent(am);
+          const float step = pow2f(-E);
+          if (live) {
+            uint8_t* qrow = a.out_q + (size_t)(row0 + m) * a.F + col0;
+            qrow[cl] = (uint8_t)mx_encode(h[0], step);
+            qrow[16 + cl] = (uint8_t)mx_encode(h[1], step);
+            if (cl == 0) a.out_s[(size_t)(row0 + m) * (a.F / 32) + col0 / 32] = (uint8_t)(E + 127);
+          }
+        } else if (live) {
+#pragma unroll
+          for (int c = 0; c < 2; c++) a.out[(size_t)(row0 + m) * a.F + col0 + 16 * c + cl] = h[c];
         }
       }
   } else {

@@ -62,6 +62,11 @@ struct GemmArgs {
   int cap_form;
   float cap;
   float* out;              // gate/up: h [P][F]; down: y [P][H] (rows in sorted order)
+  // MXFP8 gate/up only: h is encoded in the epilogue (each workgroup's
+  // columns of a row are whole 32-element blocks) into codes [P][F] and E8M0
+  // scales [P][F/32] instead of being written to `out`
+  uint8_t* out_q;
+  uint8_t* out_s;
 };
 int gemm_tile_m(int T, int k, int E);
 // LDS-staged variant for 128-row work-list entries (gemm_big.hip); needs

@@ -85,6 +85,10 @@ __host__ __device__ inline int mx_exponent(float amax) {
   return e < -127 ? -127 : e;
 }
 
+// One MXFP8 element given its block's step 2^-E (E = mx_exponent(amax)):
+// the scaling is exact, the encode rounds once.
+__device__ inline uint32_t mx_encode(float v, float step) { return e4m3_encode(__fmul_rn(v, step)); }
+
 __device__ inline float bf16_to_f32(uint16_t h) { return bits_f((uint32_t)h << 16); }
 
 // fp32 -> bf16, round to nearest even (finite inputs).
