@@ -3,20 +3,22 @@
 // (SGLang cookbook "Inkling-2-Small" section 2, "MegaMoE" and "Checkpoints";
 // Miles docs section 5.3).
 //
-// Workgroup: 8 waves, tile of 128 rows (a dispatch work-list entry with
-// tile_m = 128) x 256 weight rows, k step 128.  Waves form 2 (rows) x 4
-// (weight rows); each owns a 64 x 64 block of sixteen 16x16 MFMA tiles.
+// Both kernels: workgroup of 8 waves, tile of 128 rows (a dispatch work-list
+// entry with tile_m = 128) x 256 weight rows, k step 128.
 //  - The activation tile of each k step is staged through LDS once per
-//    workgroup (double-buffered, one barrier per step) and shared by the four
-//    waves of each row half.  NVFP4 activations are expanded to f16 (code *
-//    block scale, exact) while they are written to LDS, so the expansion is
-//    paid once per workgroup; MXFP8 activations stay E4M3 with their E8M0
-//    scales.
-//  - Each wave streams its own 64 weight rows straight from HBM into MFMA
+//    workgroup (double-buffered, one barrier per step), in MFMA lane order
+//    so every wavefront store and load is 1 KB contiguous.  NVFP4
+//    activations are expanded to f16 (code * block scale, exact) while they
+//    are written to LDS; MXFP8 activations stay E4M3 with their E8M0 scales.
+//  - Each wave streams its own weight rows straight from HBM into MFMA
 //    operand registers through a ring of PF k steps (the packed tile layout:
 //    one contiguous kilobyte per wavefront load; the canonical layout works
-//    too, with 64-byte row pieces).  NVFP4 weight fragments are expanded in
-//    registers as in the decode kernel.
+//    too, with 64-byte row pieces).
+//  - MXFP8 (k_expert_gemm_big): waves form 2 (rows) x 4 (weight rows), each
+//    a 64 x 64 block; the gate/up epilogue encodes h to MXFP8 directly.
+//  - NVFP4 (k_expert_gemm_big_nv): waves form 1 x 8, each all 128 rows x 32
+//    weight rows, so each weight fragment is expanded to f16 once per
+//    workgroup (see there).
 // Each weight element is fetched once per 128 rows of an expert; the
 // activation tile once per 256 weight rows.  Work items (row tile, weight
 // tile) are ordered so that the items one XCD runs back to back are
@@ -355,6 +357,193 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   }
 }
 
+// NVFP4 variant: the same tile (128 rows x 256 weight rows, 8 waves, k step
+// 128, activations expanded to f16 once per workgroup in LDS) but the waves
+// form 1 (rows) x 8 (weight rows): each wave owns all 128 rows x 32 weight
+// rows (8 x 2 MFMA tiles).  The exact NVFP4 path is limited by vector-ALU
+// issue (operand expansion shares issue slots with the MFMAs); here every
+// weight fragment is expanded once per workgroup and feeds 8 MFMAs, half the
+// expansion work per MFMA of the 2 x 4 arrangement, for twice the LDS reads
+// (about half of gfx950's LDS bandwidth at the MFMA rate).  The next part's
+// activation fragments are read from LDS while the current part's MFMAs run.
+template <bool PACKED, int STAGE, int PF>
+__global__ __launch_bounds__(512) void k_expert_gemm_big_nv(GemmArgs a) {
+  static_assert(PF >= 1 && PF <= 3, "ring depth");
+  constexpr int ABUF = abuf_bytes<1>();
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int tok[BM];
+  __shared__ float rgs[BM];
+
+  // XCD-aware order as in k_expert_gemm_big
+  const int nt = a.ntiles[0], nx = STAGE == 0 ? a.F / 128 : a.H / BNW;
+  const int items = nx * nt;
+  const int hw = blockIdx.x;
+  if (hw >= items) return;
+  const int q8 = items / 8, r8 = items % 8, xcd = hw % 8;
+  const int L = xcd * q8 + min(xcd, r8) + hw / 8;
+  const int tile = L % nt, bx = L / nt;
+  const int el = a.worklist[2 * tile], m0 = a.worklist[2 * tile + 1];
+  const int row0 = a.offsets[el] + m0;
+  const int rows = min(BM, a.offsets[el + 1] - row0);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int K = STAGE == 0 ? a.H : a.F;
+  const int NS = K / 128;
+  const int NW = STAGE == 0 ? 2 * a.F : a.H;
+  const int row_bytes = K / 2, sc_bytes = K / 16;
+  const uint8_t* wexp = a.w_codes + (size_t)el * NW * row_bytes;
+  const uint8_t* wsexp = a.w_sc + (size_t)el * NW * sc_bytes;
+
+  if (tid < BM) {
+    const int tk = tid < rows ? (STAGE == 0 ? a.sorted[row0 + tid] / a.k : row0 + tid) : -1;
+    tok[tid] = tk;
+    rgs[tid] = tk >= 0 ? a.a_gs[tk] : 0.0f;
+  }
+  __syncthreads();
+
+  // activation staging exactly as in k_expert_gemm_big (wave w: row tile w;
+  // NVFP4 expanded to f16 on the way into LDS)
+  const int ar = 16 * wave + r, aq = g;
+  const int at = tok[ar] >= 0 ? tok[ar] : tok[0];
+  const uint8_t* acode = a.a_codes + (size_t)at * row_bytes + 16 * aq;
+  const uint8_t* asc = a.a_sc + (size_t)at * sc_bytes + 2 * aq;
+  auto aload = [&](int s, AStage4& st) {
+    st.q = *reinterpret_cast<const v4u*>(acode + s * 64);
+    st.sc = *reinterpret_cast<const uint16_t*>(asc + s * 8);
+  };
+  auto astore = [&](int buf, const AStage4& st) {
+    const v2h sp = sig2_of(st.sc);
+    const v2h s0 = v2h{sp[0], sp[0]}, s1 = v2h{sp[1], sp[1]};
+    uint8_t* base = lds + buf * ABUF + wave * 4096 + lane * 16;
+    *reinterpret_cast<v8h*>(base + 0 * 1024) = dq8(st.q.x, s0);
+    *reinterpret_cast<v8h*>(base + 1 * 1024) = dq8(st.q.y, s0);
+    *reinterpret_cast<v8h*>(base + 2 * 1024) = dq8(st.q.z, s1);
+    *reinterpret_cast<v8h*>(base + 3 * 1024) = dq8(st.q.w, s1);
+  };
+
+  // this wave's two column groups of 16 weight rows: gate/up: the gate group
+  // and its up group (h columns bx*128 + 16 w ..); down: rows bx*256 + 32 w + 16 c
+  const uint8_t* brow[2];
+  const uint8_t* bsrow[2];
+#pragma unroll
+  for (int c = 0; c < 2; c++) {
+    const int n0 = STAGE == 0 ? c * a.F + bx * 128 + 16 * wave : bx * BNW + 32 * wave + 16 * c;
+    if (PACKED) {
+      const size_t t0 = (size_t)(n0 / 16) * NS;
+      brow[c] = wexp + t0 * 1024 + 16 * lane;
+      bsrow[c] = wsexp + t0 * 128 + 2 * lane;
+    } else {
+      brow[c] = wexp + (size_t)(n0 + r) * row_bytes + 16 * g;
+      bsrow[c] = wsexp + (size_t)(n0 + r) * sc_bytes + 2 * g;
+    }
+  }
+  auto bload = [&](int s, BFrag4* B) {
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      B[c].q = *reinterpret_cast<const v4u*>(brow[c] + (PACKED ? (size_t)s * 1024 : (size_t)s * 64));
+      B[c].sc = *reinterpret_cast<const uint16_t*>(bsrow[c] + (PACKED ? s * 128 : s * 8));
+    }
+  };
+
+  v4f acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; i++) acc[i][0] = acc[i][1] = v4f{0, 0, 0, 0};
+
+  auto compute = [&](int buf, const BFrag4* B) {
+    const uint8_t* A = lds + buf * ABUF;
+    v2h bs[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      const v2h sp = sig2_of(B[c].sc);
+      bs[c][0] = v2h{sp[0], sp[0]};
+      bs[c][1] = v2h{sp[1], sp[1]};
+    }
+    v8h av[2][8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) av[0][i] = *reinterpret_cast<const v8h*>(A + i * 4096 + lane * 16);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      if (j < 3) {
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          av[(j + 1) & 1][i] = *reinterpret_cast<const v8h*>(A + i * 4096 + (j + 1) * 1024 + lane * 16);
+      }
+      v8h bv[2];
+#pragma unroll
+      for (int c = 0; c < 2; c++) {
+        const uint32_t w = j == 0 ? B[c].q.x : j == 1 ? B[c].q.y : j == 2 ? B[c].q.z : B[c].q.w;
+        bv[c] = dq8(w, bs[c][j >> 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int c = 0; c < 2; c++)
+          acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[j & 1][i], bv[c], acc[i][c], 0, 0, 0);
+    }
+  };
+
+  // main loop: PF steps of weights and activations in flight (as in
+  // k_expert_gemm_big; ring slots are compile-time constants)
+  BFrag4 bring[PF][2];
+  AStage4 ast[PF];
+#pragma unroll
+  for (int j = 0; j < PF; j++) {
+    bload(min(j, NS - 1), bring[j]);
+    aload(min(j, NS - 1), ast[j]);
+  }
+  astore(0, ast[0]);
+  aload(min(PF, NS - 1), ast[0]);
+  __syncthreads();
+  auto one_step = [&](auto J, int s0) {
+    constexpr int j = decltype(J)::value;
+    const int step = s0 + j;
+    compute(step & 1, bring[j]);
+    bload(min(step + PF, NS - 1), bring[j]);
+    astore((step + 1) & 1, ast[(j + 1) % PF]);
+    aload(min(step + 1 + PF, NS - 1), ast[(j + 1) % PF]);
+    __syncthreads();
+  };
+  for (int s0 = 0; s0 < NS; s0 += PF) {
+    one_step(std::integral_constant<int, 0>{}, s0);
+    if constexpr (PF > 1) one_step(std::integral_constant<int, 1>{}, s0);
+    if constexpr (PF > 2) one_step(std::integral_constant<int, 2>{}, s0);
+  }
+
+  // epilogue: acc reg q of lane l in tile (i, c): row 16 i + 4 (l/16) + q,
+  // weight row 16 * (group c) + l%16
+  const int cl = lane & 15, g4 = lane >> 4;
+  if (STAGE == 0) {
+    const float inv_c = 1.0f / a.cap;
+    const float wg = a.w_gs[3 * el + 0], wu = a.w_gs[3 * el + 1];
+    const int col = bx * 128 + 16 * wave + cl;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int m = 16 * i + 4 * g4 + q;
+        if (m >= rows) continue;
+        const float ga = rgs[m];
+        const float gv = (acc[i][0][q] * ga) * wg;
+        const float uv = (acc[i][1][q] * ga) * wu;
+        a.out[(size_t)(row0 + m) * a.F + col] = cap_swiglu(gv, uv, a.cap_form, a.cap, inv_c);
+      }
+  } else {
+    const float wd = a.w_gs[3 * el + 2];
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int m = 16 * i + 4 * g4 + q;
+        if (m >= rows) continue;
+        const float ha = rgs[m];
+#pragma unroll
+        for (int c = 0; c < 2; c++)
+          a.out[(size_t)(row0 + m) * a.H + bx * BNW + 32 * wave + 16 * c + cl] = (acc[i][c][q] * ha) * wd;
+      }
+  }
+}
+
 namespace {
 
 template <int FMT, int ST, bool PK, int PF>
@@ -369,11 +558,28 @@ void launch_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL((k_expert_gemm_big<FMT, ST, PK, PF>), grid, dim3(WAVES * 64), lds, stream, a);
 }
 
+template <int ST, bool PK, int PF>
+void launch_nv_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  const size_t lds = 2 * abuf_bytes<1>();
+  static bool done = false;   // dynamic LDS above 64 KiB must be allowed once
+  if (!done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm_big_nv<PK, ST, PF>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    done = true;
+  }
+  hipLaunchKernelGGL((k_expert_gemm_big_nv<PK, ST, PF>), grid, dim3(WAVES * 64), lds, stream, a);
+}
+
 template <int FMT, int ST, bool PK>
 void launch_pf(const GemmArgs& a, dim3 grid, hipStream_t stream) {
   const int ns = (ST == 0 ? a.H : a.F) / 128;
-  if (ns % 2 == 0) launch_one<FMT, ST, PK, 2>(a, grid, stream);
-  else launch_one<FMT, ST, PK, 1>(a, grid, stream);
+  if constexpr (FMT == 1) {
+    if (ns % 2 == 0) launch_nv_one<ST, PK, 2>(a, grid, stream);
+    else launch_nv_one<ST, PK, 1>(a, grid, stream);
+  } else {
+    if (ns % 2 == 0) launch_one<FMT, ST, PK, 2>(a, grid, stream);
+    else launch_one<FMT, ST, PK, 1>(a, grid, stream);
+  }
 }
 
 }  // namespace
