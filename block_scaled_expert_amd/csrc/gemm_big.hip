@@ -75,15 +75,12 @@ constexpr int abuf_bytes() {
 
 }  // namespace
 
-template <int FMT, int STAGE, bool PACKED, int PF>
+template <int STAGE, bool PACKED, int PF>
 __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   static_assert(PF >= 1 && PF <= 3, "ring depth");
-  typedef typename std::conditional<FMT == 2, BFrag8, BFrag4>::type BFrag;
-  typedef typename std::conditional<FMT == 2, AStage8, AStage4>::type AStage;
-  constexpr int ABUF = abuf_bytes<FMT>();
+  constexpr int ABUF = abuf_bytes<2>();
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int tok[BM];
-  __shared__ float rgs[BM];
 
   // XCD-aware order: work item L = (weight tile L / nt, row tile L % nt);
   // consecutive items of one XCD are consecutive row tiles of one weight tile
@@ -104,18 +101,11 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   const int K = STAGE == 0 ? a.H : a.F;
   const int NS = K / 128;
   const int NW = STAGE == 0 ? 2 * a.F : a.H;
-  const int row_bytes = FMT == 2 ? K : K / 2;
-  const int sc_bytes = FMT == 2 ? K / 32 : K / 16;
+  const int row_bytes = K, sc_bytes = K / 32;
   const uint8_t* wexp = a.w_codes + (size_t)el * NW * row_bytes;
   const uint8_t* wsexp = a.w_sc + (size_t)el * NW * sc_bytes;
 
-  // token of each row and (NVFP4) its activation row scale, read once here:
-  // a load under the epilogue's row test would wait for memory once per row
-  if (tid < BM) {
-    const int tk = tid < rows ? (STAGE == 0 ? a.sorted[row0 + tid] / a.k : row0 + tid) : -1;
-    tok[tid] = tk;
-    if (FMT == 1) rgs[tid] = tk >= 0 ? a.a_gs[tk] : 0.0f;
-  }
+  if (tid < BM) tok[tid] = tid < rows ? (STAGE == 0 ? a.sorted[row0 + tid] / a.k : row0 + tid) : -1;
   __syncthreads();
 
   // ---- activation staging ------------------------------------------------
@@ -126,39 +116,22 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   const int at = tok[ar] >= 0 ? tok[ar] : tok[0];     // rows past the tile: outputs discarded
   const uint8_t* acode = a.a_codes + (size_t)at * row_bytes;
   const uint8_t* asc = a.a_sc + (size_t)at * sc_bytes;
-  auto aload = [&](int s, AStage& st) {
-    if constexpr (FMT == 1) {
-      st.q = *reinterpret_cast<const v4u*>(acode + s * 64 + 16 * aq);
-      st.sc = *reinterpret_cast<const uint16_t*>(asc + s * 8 + 2 * aq);
-    } else {
-      const v4u* p = reinterpret_cast<const v4u*>(acode + s * 128 + 32 * aq);
-      st.lo = p[0];
-      st.hi = p[1];
-      st.sc = asc[s * 4 + aq];
-    }
+  auto aload = [&](int s, AStage8& st) {
+    const v4u* p = reinterpret_cast<const v4u*>(acode + s * 128 + 32 * aq);
+    st.lo = p[0];
+    st.hi = p[1];
+    st.sc = asc[s * 4 + aq];
   };
-  auto astore = [&](int buf, const AStage& st) {
+  auto astore = [&](int buf, const AStage8& st) {
     uint8_t* A = lds + buf * ABUF;
     const int f = ar >> 4, rr = ar & 15;
-    if constexpr (FMT == 1) {
-      // column group g = aq of row rr is lane rr + 16 aq; MFMA part j takes
-      // its elements 8j..8j+7; stored [tile f][part j][lane], f16 x 8 each
-      const v2h sp = sig2_of(st.sc);
-      const v2h s0 = v2h{sp[0], sp[0]}, s1 = v2h{sp[1], sp[1]};
-      uint8_t* base = A + f * 4096 + (rr + 16 * aq) * 16;
-      *reinterpret_cast<v8h*>(base + 0 * 1024) = dq8(st.q.x, s0);
-      *reinterpret_cast<v8h*>(base + 1 * 1024) = dq8(st.q.y, s0);
-      *reinterpret_cast<v8h*>(base + 2 * 1024) = dq8(st.q.z, s1);
-      *reinterpret_cast<v8h*>(base + 3 * 1024) = dq8(st.q.w, s1);
-    } else {
-      // bytes [32 aq, +32) of the row's step are column groups 2(aq%2) and
-      // 2(aq%2)+1: their first halves for aq < 2, second halves for aq >= 2
-      const int h = aq >> 1, g0 = 2 * (aq & 1);
-      uint8_t* T = A + f * 2112;
-      *reinterpret_cast<v4u*>(T + 1024 * h + (rr + 16 * g0) * 16) = st.lo;
-      *reinterpret_cast<v4u*>(T + 1024 * h + (rr + 16 * (g0 + 1)) * 16) = st.hi;
-      T[2048 + rr + 16 * aq] = (uint8_t)st.sc;
-    }
+    // bytes [32 aq, +32) of the row's step are column groups 2(aq%2) and
+    // 2(aq%2)+1: their first halves for aq < 2, second halves for aq >= 2
+    const int h = aq >> 1, g0 = 2 * (aq & 1);
+    uint8_t* T = A + f * 2112;
+    *reinterpret_cast<v4u*>(T + 1024 * h + (rr + 16 * g0) * 16) = st.lo;
+    *reinterpret_cast<v4u*>(T + 1024 * h + (rr + 16 * (g0 + 1)) * 16) = st.hi;
+    T[2048 + rr + 16 * aq] = (uint8_t)st.sc;
   };
 
   // ---- weight fragments of this wave (4 column groups of 16 weight rows) ---
@@ -173,36 +146,25 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
       n0 = bx * BNW + 64 * wn + 16 * c;
     if (PACKED) {
       const size_t t0 = (size_t)(n0 / 16) * NS;
-      brow[c] = wexp + t0 * (FMT == 2 ? 2048 : 1024);
-      bsrow[c] = wsexp + t0 * (FMT == 2 ? 64 : 128);
+      brow[c] = wexp + t0 * 2048;
+      bsrow[c] = wsexp + t0 * 64;
     } else {
       brow[c] = wexp + (size_t)(n0 + r) * row_bytes;
       bsrow[c] = wsexp + (size_t)(n0 + r) * sc_bytes;
     }
   }
-  auto bload = [&](int s, BFrag* B) {
+  auto bload = [&](int s, BFrag8* B) {
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      if constexpr (FMT == 1) {
-        if (PACKED) {
-          B[c].q = *reinterpret_cast<const v4u*>(brow[c] + (size_t)s * 1024 + 16 * lane);
-          B[c].sc = *reinterpret_cast<const uint16_t*>(bsrow[c] + s * 128 + 2 * lane);
-        } else {
-          B[c].q = *reinterpret_cast<const v4u*>(brow[c] + s * 64 + 16 * g);
-          const uint8_t* sp = bsrow[c] + s * 8 + 2 * g;
-          B[c].sc = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
-        }
+      if (PACKED) {
+        const uint8_t* t = brow[c] + (size_t)s * 2048 + 16 * lane;
+        B[c].lo = *reinterpret_cast<const v4u*>(t);
+        B[c].hi = *reinterpret_cast<const v4u*>(t + 1024);
+        B[c].sc = bsrow[c][s * 64 + lane];
       } else {
-        if (PACKED) {
-          const uint8_t* t = brow[c] + (size_t)s * 2048 + 16 * lane;
-          B[c].lo = *reinterpret_cast<const v4u*>(t);
-          B[c].hi = *reinterpret_cast<const v4u*>(t + 1024);
-          B[c].sc = bsrow[c][s * 64 + lane];
-        } else {
-          B[c].lo = *reinterpret_cast<const v4u*>(brow[c] + s * 128 + 16 * g);
-          B[c].hi = *reinterpret_cast<const v4u*>(brow[c] + s * 128 + 64 + 16 * g);
-          B[c].sc = bsrow[c][s * 4 + g];
-        }
+        B[c].lo = *reinterpret_cast<const v4u*>(brow[c] + s * 128 + 16 * g);
+        B[c].hi = *reinterpret_cast<const v4u*>(brow[c] + s * 128 + 64 + 16 * g);
+        B[c].sc = bsrow[c][s * 4 + g];
       }
     }
   };
@@ -213,50 +175,24 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; c++) acc[i][c] = v4f{0, 0, 0, 0};
 
-  auto compute = [&](int buf, const BFrag* B) {
+  auto compute = [&](int buf, const BFrag8* B) {
     const uint8_t* A = lds + buf * ABUF;
-    if constexpr (FMT == 1) {
-      v2h bs[4][2];
+    v8i bv[4];
 #pragma unroll
-      for (int c = 0; c < 4; c++) {
-        const v2h sp = sig2_of(B[c].sc);
-        bs[c][0] = v2h{sp[0], sp[0]};
-        bs[c][1] = v2h{sp[1], sp[1]};
-      }
+    for (int c = 0; c < 4; c++)
+      bv[c] = v8i{(int)B[c].lo.x, (int)B[c].lo.y, (int)B[c].lo.z, (int)B[c].lo.w,
+                  (int)B[c].hi.x, (int)B[c].hi.y, (int)B[c].hi.z, (int)B[c].hi.w};
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        v8h bv[4];
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-          const uint32_t w = j == 0 ? B[c].q.x : j == 1 ? B[c].q.y : j == 2 ? B[c].q.z : B[c].q.w;
-          bv[c] = dq8(w, bs[c][j >> 1]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const v8h av = *reinterpret_cast<const v8h*>(A + (4 * wm + i) * 4096 + j * 1024 + lane * 16);
-#pragma unroll
-          for (int c = 0; c < 4; c++)
-            acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[c], acc[i][c], 0, 0, 0);
-        }
-      }
-    } else {
-      v8i bv[4];
+    for (int i = 0; i < 4; i++) {
+      const uint8_t* T = A + (4 * wm + i) * 2112;
+      const v4u lo = *reinterpret_cast<const v4u*>(T + 16 * lane);
+      const v4u hi = *reinterpret_cast<const v4u*>(T + 1024 + 16 * lane);
+      const v8i av = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const int as = T[2048 + lane];
 #pragma unroll
       for (int c = 0; c < 4; c++)
-        bv[c] = v8i{(int)B[c].lo.x, (int)B[c].lo.y, (int)B[c].lo.z, (int)B[c].lo.w,
-                    (int)B[c].hi.x, (int)B[c].hi.y, (int)B[c].hi.z, (int)B[c].hi.w};
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const uint8_t* T = A + (4 * wm + i) * 2112;
-        const v4u lo = *reinterpret_cast<const v4u*>(T + 16 * lane);
-        const v4u hi = *reinterpret_cast<const v4u*>(T + 1024 + 16 * lane);
-        const v8i av = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        const int as = T[2048 + lane];
-#pragma unroll
-        for (int c = 0; c < 4; c++)
-          acc[i][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[c], acc[i][c], 0, 0, 0, as, 0,
-                                                                       (int)B[c].sc);
-      }
+        acc[i][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[c], acc[i][c], 0, 0, 0, as, 0,
+                                                                     (int)B[c].sc);
     }
   };
 
@@ -264,8 +200,8 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   // NS is a multiple of PF; slot j holds the steps congruent to j mod PF.
   // No load sits under a branch (see gemm.hip); past the end a step is
   // re-read, harmlessly.
-  BFrag bring[PF][4];
-  AStage ast[PF];
+  BFrag8 bring[PF][4];
+  AStage8 ast[PF];
 #pragma unroll
   for (int j = 0; j < PF; j++) {
     bload(min(j, NS - 1), bring[j]);
@@ -298,61 +234,40 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   const int cl = lane & 15, g4 = lane >> 4;
   if (STAGE == 0) {
     const float inv_c = 1.0f / a.cap;
-    const float wg = FMT == 1 ? a.w_gs[3 * el + 0] : 1.0f;
-    const float wu = FMT == 1 ? a.w_gs[3 * el + 1] : 1.0f;
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 64 * wm + 16 * i + 4 * g4 + q;
         const bool live = m < rows;
-        const float ga = FMT == 1 ? rgs[m] : 1.0f;
         float h[2];
 #pragma unroll
-        for (int c = 0; c < 2; c++) {
-          float gv = acc[i][c][q], uv = acc[i][c + 2][q];
-          if (FMT == 1) {
-            gv = (gv * ga) * wg;
-            uv = (uv * ga) * wu;
-          }
-          h[c] = cap_swiglu(gv, uv, a.cap_form, a.cap, inv_c);
-        }
+        for (int c = 0; c < 2; c++) h[c] = cap_swiglu(acc[i][c][q], acc[i][c + 2][q], a.cap_form, a.cap, inv_c);
+        // the wave's 32 columns of row m (16 lanes x 2 groups) are one MX
+        // block: amax across the 16 lanes of this row, then each lane
+        // encodes its two values; all lanes take part in the exchange
         const int col0 = bx * 128 + 32 * wn;
-        if (FMT == 2) {
-          // the wave's 32 columns of row m (16 lanes x 2 groups) are one MX
-          // block: amax across the 16 lanes of this row, then each lane
-          // encodes its two values; all lanes take part in the exchange
-          float am = live ? fmaxf(fabsf(h[0]), fabsf(h[1])) : 0.0f;
+        float am = live ? fmaxf(fabsf(h[0]), fabsf(h[1])) : 0.0f;
 #pragma unroll
-          for (int o = 8; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, kWave));
-          const int E = mx_exponent(am);
-          const float step = pow2f(-E);
-          if (live) {
-            uint8_t* qrow = a.out_q + (size_t)(row0 + m) * a.F + col0;
-            qrow[cl] = (uint8_t)mx_encode(h[0], step);
-            qrow[16 + cl] = (uint8_t)mx_encode(h[1], step);
-            if (cl == 0) a.out_s[(size_t)(row0 + m) * (a.F / 32) + col0 / 32] = (uint8_t)(E + 127);
-          }
-        } else if (live) {
-#pragma unroll
-          for (int c = 0; c < 2; c++) a.out[(size_t)(row0 + m) * a.F + col0 + 16 * c + cl] = h[c];
+        for (int o = 8; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, kWave));
+        const int E = mx_exponent(am);
+        const float step = pow2f(-E);
+        if (live) {
+          uint8_t* qrow = a.out_q + (size_t)(row0 + m) * a.F + col0;
+          qrow[cl] = (uint8_t)mx_encode(h[0], step);
+          qrow[16 + cl] = (uint8_t)mx_encode(h[1], step);
+          if (cl == 0) a.out_s[(size_t)(row0 + m) * (a.F / 32) + col0 / 32] = (uint8_t)(E + 127);
         }
       }
   } else {
-    const float wd = FMT == 1 ? a.w_gs[3 * el + 2] : 1.0f;
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 64 * wm + 16 * i + 4 * g4 + q;
         if (m >= rows) continue;
-        const float ha = FMT == 1 ? rgs[m] : 1.0f;
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-          float yv = acc[i][c][q];
-          if (FMT == 1) yv = (yv * ha) * wd;
-          a.out[(size_t)(row0 + m) * a.H + bx * BNW + 64 * wn + 16 * c + cl] = yv;
-        }
+        for (int c = 0; c < 4; c++) a.out[(size_t)(row0 + m) * a.H + bx * BNW + 64 * wn + 16 * c + cl] = acc[i][c][q];
       }
   }
 }
@@ -546,16 +461,10 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_nv(GemmArgs a) {
 
 namespace {
 
-template <int FMT, int ST, bool PK, int PF>
-void launch_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  const size_t lds = 2 * abuf_bytes<FMT>();
-  static bool done = false;   // dynamic LDS above 64 KiB must be allowed once
-  if (!done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm_big<FMT, ST, PK, PF>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    done = true;
-  }
-  hipLaunchKernelGGL((k_expert_gemm_big<FMT, ST, PK, PF>), grid, dim3(WAVES * 64), lds, stream, a);
+template <int ST, bool PK, int PF>
+void launch_mx_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
+  const size_t lds = 2 * abuf_bytes<2>();
+  hipLaunchKernelGGL((k_expert_gemm_big<ST, PK, PF>), grid, dim3(WAVES * 64), lds, stream, a);
 }
 
 template <int ST, bool PK, int PF>
@@ -577,8 +486,8 @@ void launch_pf(const GemmArgs& a, dim3 grid, hipStream_t stream) {
     if (ns % 2 == 0) launch_nv_one<ST, PK, 2>(a, grid, stream);
     else launch_nv_one<ST, PK, 1>(a, grid, stream);
   } else {
-    if (ns % 2 == 0) launch_one<FMT, ST, PK, 2>(a, grid, stream);
-    else launch_one<FMT, ST, PK, 1>(a, grid, stream);
+    if (ns % 2 == 0) launch_mx_one<ST, PK, 2>(a, grid, stream);
+    else launch_mx_one<ST, PK, 1>(a, grid, stream);
   }
 }
 
