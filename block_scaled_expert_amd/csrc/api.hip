@@ -239,13 +239,6 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   const bool nv = c->fmt == MOE_FMT_NVFP4;
   int bad = 0;
 
-  // 1. quantize x per row
-  record(events, 2 * MOE_STAGE_QUANT_X, s);
-  bad |= launch_quant(c->fmt, 0, x, T, nullptr, H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs),
-                      at<float>(ws, L.xg), s);
-  record(events, 2 * MOE_STAGE_QUANT_X + 1, s);
-
-  // 2. dispatch + tile list
   int tile_m = gemm_tile_m(T, k, c->num_experts);
   if (tile_m == 128 && !gemm_big_supported(H, F)) tile_m = 64;
   DispatchBufs b;
@@ -255,9 +248,27 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   b.pos = at<int32_t>(ws, L.pos);
   b.worklist = at<int32_t>(ws, L.work);
   b.ntiles = at<int32_t>(ws, L.ntiles);
-  record(events, 2 * MOE_STAGE_DISPATCH, s);
-  bad |= launch_dispatch(topk_ids, P, c->expert_begin, EL, tile_m, b, s);
-  record(events, 2 * MOE_STAGE_DISPATCH + 1, s);
+  if (P <= kSmallDispatchPairs) {
+    // 1 + 2. quantize x per row and dispatch (+ tile list) in one launch; the
+    // quantize-x stage covers both, the dispatch stage is empty
+    record(events, 2 * MOE_STAGE_QUANT_X, s);
+    bad |= launch_prep_small(c->fmt, static_cast<const uint16_t*>(x), T, H, at<uint8_t>(ws, L.xq),
+                             at<uint8_t>(ws, L.xs), at<float>(ws, L.xg), topk_ids, P, c->expert_begin, EL, tile_m,
+                             b, s);
+    record(events, 2 * MOE_STAGE_QUANT_X + 1, s);
+    record(events, 2 * MOE_STAGE_DISPATCH, s);
+    record(events, 2 * MOE_STAGE_DISPATCH + 1, s);
+  } else {
+    // 1. quantize x per row
+    record(events, 2 * MOE_STAGE_QUANT_X, s);
+    bad |= launch_quant(c->fmt, 0, x, T, nullptr, H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs),
+                        at<float>(ws, L.xg), s);
+    record(events, 2 * MOE_STAGE_QUANT_X + 1, s);
+    // 2. dispatch + tile list
+    record(events, 2 * MOE_STAGE_DISPATCH, s);
+    bad |= launch_dispatch(topk_ids, P, c->expert_begin, EL, tile_m, b, s);
+    record(events, 2 * MOE_STAGE_DISPATCH + 1, s);
+  }
 
   // 3. gate/up GEMM + capped SwiGLU -> h (fp32, sorted rows)
   GemmArgs g;

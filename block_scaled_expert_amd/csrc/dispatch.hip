@@ -16,6 +16,7 @@
 //           position; integer atomics only accumulate counts.
 #include "moe_common.h"
 #include "launch.h"
+#include "quant_row.h"
 
 namespace moe {
 
@@ -156,13 +157,13 @@ __global__ __launch_bounds__(256) void k_disp_scatter(const int32_t* __restrict_
 // expert; a pair's rank is the number of such lanes below it plus the pairs
 // of that expert placed before its wavefront, which the wavefronts add to a
 // running per-expert count in wavefront order.
-constexpr int kSmallP = 4096;
+constexpr int kSmallP = kSmallDispatchPairs;
 
-__global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__ ids, int P, int E_begin,
-                                                     int E_local, int tile_m, int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
-                                                     int32_t* __restrict__ worklist,
-                                                     int32_t* __restrict__ ntiles) {
+// Body of the small-batch dispatch for one workgroup of 1024 threads.
+__device__ inline void disp_small_body(const int32_t* __restrict__ ids, int P, int E_begin, int E_local,
+                                       int tile_m, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+                                       int32_t* __restrict__ pos, int32_t* __restrict__ worklist,
+                                       int32_t* __restrict__ ntiles) {
   __shared__ int32_t cnt[1024], off[1024], toff[1024];
   const int i = threadIdx.x, wave = i >> 6, lane = i & 63;
   cnt[i] = 0;
@@ -225,6 +226,56 @@ __global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__
       __syncthreads();
     }
   }
+}
+
+__global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__ ids, int P, int E_begin,
+                                                     int E_local, int tile_m, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ sorted, int32_t* __restrict__ pos,
+                                                     int32_t* __restrict__ worklist,
+                                                     int32_t* __restrict__ ntiles) {
+  disp_small_body(ids, P, E_begin, E_local, tile_m, offsets, sorted, pos, worklist, ntiles);
+}
+
+// Small batches, one launch for two independent steps of the forward:
+// workgroup 0 dispatches the pairs, workgroups 1.. quantize the bf16 token
+// rows (4 rows each, one per group of 256 threads).
+template <int FMT>
+__global__ __launch_bounds__(1024) void k_prep_small(const uint16_t* __restrict__ x, int T, int H,
+                                                     uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+                                                     float* __restrict__ xg, const int32_t* __restrict__ ids,
+                                                     int P, int E_begin, int E_local, int tile_m,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+                                                     int32_t* __restrict__ pos, int32_t* __restrict__ worklist,
+                                                     int32_t* __restrict__ ntiles) {
+  if (blockIdx.x == 0) {
+    disp_small_body(ids, P, E_begin, E_local, tile_m, offsets, sorted, pos, worklist, ntiles);
+    return;
+  }
+  __shared__ float red[4][4];
+  const int grp = threadIdx.x >> 8, t = threadIdx.x & 255;
+  const int row = (blockIdx.x - 1) * 4 + grp;
+  const bool live = row < T;
+  const int rr = live ? row : T - 1;   // every group takes the barrier; only live rows write
+  const uint16_t* xr = x + (size_t)rr * H;
+  if (FMT == 1)
+    quant_row_nvfp4<uint16_t>(xr, H, t, red[grp], live, xq + (size_t)rr * (H / 2), xs + (size_t)rr * (H / 16),
+                              xg + rr);
+  else
+    quant_row_mxfp8<uint16_t>(xr, H, t, live, xq + (size_t)rr * H, xs + (size_t)rr * (H / 32));
+}
+
+int launch_prep_small(int fmt, const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs, float* xg,
+                      const int32_t* ids, int P, int E_begin, int E_local, int tile_m, const DispatchBufs& b,
+                      hipStream_t stream) {
+  if (P > kSmallP || T <= 0) return -1;
+  const dim3 grid(1 + ceil_div(T, 4));
+  if (fmt == 1)
+    hipLaunchKernelGGL(k_prep_small<1>, grid, dim3(1024), 0, stream, x, T, H, xq, xs, xg, ids, P, E_begin, E_local,
+                       tile_m, b.offsets, b.sorted, b.pos, b.worklist, b.ntiles);
+  else
+    hipLaunchKernelGGL(k_prep_small<2>, grid, dim3(1024), 0, stream, x, T, H, xq, xs, xg, ids, P, E_begin, E_local,
+                       tile_m, b.offsets, b.sorted, b.pos, b.worklist, b.ntiles);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_dispatch(const int32_t* ids, int P, int E_begin, int E_local, int tile_m,

@@ -37,6 +37,13 @@ struct DispatchBufs {
 int dispatch_chunk(int P);
 int launch_dispatch(const int32_t* ids, int P, int E_begin, int E_local, int tile_m,
                     const DispatchBufs& b, hipStream_t stream);
+// Pair counts up to this take one workgroup for the dispatch ...
+constexpr int kSmallDispatchPairs = 4096;
+// ... and can share a launch with the quantization of the bf16 token rows
+// (xq / xs / xg as launch_quant writes them for fmt 1 or 2).
+int launch_prep_small(int fmt, const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs, float* xg,
+                      const int32_t* ids, int P, int E_begin, int E_local, int tile_m, const DispatchBufs& b,
+                      hipStream_t stream);
 
 struct GemmArgs {
   int fmt;                 // 1 NVFP4, 2 MXFP8

@@ -230,7 +230,11 @@ int moe_prepare_weights(const moe_config* cfg, const moe_expert_weights* src, mo
  *   the local pairs (a partial sum when only some experts are local).
  *  x [T][H] bf16; out [T][H] bf16.  weights: local experts (host struct
  *  pointing at device arrays).  events: optional stage timing (host array of
- *  2*MOE_STAGE_COUNT hipEvent_t, or NULL). */
+ *  2*MOE_STAGE_COUNT hipEvent_t, or NULL; events[2s] is recorded before stage
+ *  s and events[2s+1] after it).  Stages that share a launch: with at most
+ *  4096 (token, slot) pairs, x quantization and dispatch run as one kernel,
+ *  timed by the QUANT_X pair (the DISPATCH pair is recorded back to back);
+ *  in MXFP8, h is encoded by the gate/up kernel (the QUANT_H pair is empty). */
 int moe_forward(const moe_config* cfg, const void* x, int32_t T, const int32_t* topk_ids,
                 const float* topk_w, const moe_expert_weights* weights, void* out,
                 void* ws, size_t ws_bytes, void* stream, void* const* events);
