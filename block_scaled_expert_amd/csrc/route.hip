@@ -114,15 +114,17 @@ __global__ __launch_bounds__(256) void k_router_logits_tiled(const uint16_t* __r
     ap[u] = x + (size_t)min(t0 + 16 * f + (l & 15), T - 1) * H + koff;
     bp[u] = wr + (size_t)min(e0 + 16 * f + (l & 15), E - 1) * H + koff;
   }
-  v4u sa[4], sb[4];
-  auto gload = [&](int st) {
+  // two register stages: a step's global loads are issued two steps before
+  // its MFMAs (one step before its LDS store)
+  v4u ra[2][4], rb[2][4];
+  auto gload = [&](int st, v4u (&sa)[4], v4u (&sb)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       sa[u] = *reinterpret_cast<const v4u*>(ap[u] + st * 64);
       sb[u] = *reinterpret_cast<const v4u*>(bp[u] + st * 64);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const v4u (&sa)[4], const v4u (&sb)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       *reinterpret_cast<v4u*>(&lds[buf][0][16 * (tid + 256 * u)]) = sa[u];
@@ -135,31 +137,41 @@ __global__ __launch_bounds__(256) void k_router_logits_tiled(const uint16_t* __r
   for (int i = 0; i < 4; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = v4f{0, 0, 0, 0};
-
-  if (s_hi > s_lo) {
-    gload(s_lo);
-    lstore(0);
-    gload(min(s_lo + 1, s_hi - 1));
-    __syncthreads();
-    for (int st = s_lo; st < s_hi; st++) {
-      const int buf = (st - s_lo) & 1;
+  auto mma = [&](int buf) {
 #pragma unroll
-      for (int hh = 0; hh < 2; hh++) {
-        v4u av[4], bv[4];
+    for (int hh = 0; hh < 2; hh++) {
+      v4u av[4], bv[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          av[i] = *reinterpret_cast<const v4u*>(&lds[buf][0][16 * ((4 * wm + i) * 128 + hh * 64 + lane)]);
-          bv[i] = *reinterpret_cast<const v4u*>(&lds[buf][1][16 * ((4 * wn + i) * 128 + hh * 64 + lane)]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-          for (int j = 0; j < 4; j++)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[i]),
-                                                                __builtin_bit_cast(v8bf, bv[j]), acc[i][j], 0, 0, 0);
+      for (int i = 0; i < 4; i++) {
+        av[i] = *reinterpret_cast<const v4u*>(&lds[buf][0][16 * ((4 * wm + i) * 128 + hh * 64 + lane)]);
+        bv[i] = *reinterpret_cast<const v4u*>(&lds[buf][1][16 * ((4 * wn + i) * 128 + hh * 64 + lane)]);
       }
-      lstore(buf ^ 1);                        // the buffer read one step ago
-      gload(min(st + 2, s_hi - 1));
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[i]),
+                                                              __builtin_bit_cast(v8bf, bv[j]), acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Steps s_lo + 2n use LDS buffer 0, s_lo + 2n + 1 buffer 1; a buffer is
+  // rewritten only after the barrier that follows its last read.  Loads past
+  // the slice re-read its last step; a missing odd last step is skipped.
+  if (s_hi > s_lo) {
+    gload(s_lo, ra[0], rb[0]);
+    lstore(0, ra[0], rb[0]);
+    gload(min(s_lo + 1, s_hi - 1), ra[0], rb[0]);
+    gload(min(s_lo + 2, s_hi - 1), ra[1], rb[1]);
+    __syncthreads();
+    for (int st = s_lo; st < s_hi; st += 2) {
+      mma(0);                                           // step st
+      lstore(1, ra[0], rb[0]);                          // step st + 1
+      gload(min(st + 3, s_hi - 1), ra[0], rb[0]);
+      __syncthreads();
+      if (st + 1 < s_hi) mma(1);                        // step st + 1
+      lstore(0, ra[1], rb[1]);                          // step st + 2
+      gload(min(st + 4, s_hi - 1), ra[1], rb[1]);
       __syncthreads();
     }
   }
@@ -295,11 +307,12 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ z
 }
 
 // K splits: small batches (split-K GEMV, 6 / 4 / 2 planes); larger ones
-// (128 x 128 tiles) take enough splits for about 512 workgroups, at most 6.
+// (128 x 128 tiles, two workgroups per CU) take as many splits as keep the
+// grid within 512 workgroups, at most 6.
 int router_splits(int T, int E) {
   if (T <= 256) return T <= 64 ? 6 : T <= 128 ? 4 : 2;
   const int tiles = ceil_div(T, 128) * ceil_div(E, 128);
-  return std::min(kMaxSplits, std::max(1, ceil_div(512, tiles)));
+  return std::min(kMaxSplits, std::max(1, 512 / tiles));   // one round of 512 workgroup slots
 }
 
 size_t router_z_rows(int max_tokens) { return (size_t)kMaxSplits * (size_t)std::max(max_tokens, 0); }
