@@ -75,7 +75,8 @@ def upload_weights(w, bse_cfg):
 def gemm_source(workload: str) -> str:
     """Source file of the expert GEMM kernel a workload runs: decode batches
     (a few rows per expert) take k_expert_gemm, prefill chunks and
-    expert-parallel shares (128-row tiles) take k_expert_gemm_big."""
+    expert-parallel shares (128-row tiles) take k_expert_gemm_big_nv (NVFP4)
+    or k_expert_gemm_big_mx (MXFP8)."""
     small = workload.startswith("decode") or workload == "tiny"
     return "gemm.hip" if small else "gemm_big.hip"
 
@@ -262,7 +263,8 @@ def main() -> int:
     alg_bytes = expert_bytes + E * H * 2 + E * 4 + 2 * T * H * 2
 
     decode = w.key.startswith("decode") or w.key == "tiny"
-    gemm_kernel = "k_expert_gemm" if gemm_source(w.key) == "gemm.hip" else "k_expert_gemm_big"
+    gemm_kernel = ("k_expert_gemm" if gemm_source(w.key) == "gemm.hip"
+                   else "k_expert_gemm_big_nv" if w.fmt == "nvfp4" else "k_expert_gemm_big_mx")
     if decode or w.key.startswith("ep8"):
         achieved = active * w13_bytes / (gate_up_ms * 1e-3) / 1e9
         tr = measured_traffic(w.key, "gate_up") if args.layout == "packed" else None

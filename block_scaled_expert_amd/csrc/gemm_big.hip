@@ -14,11 +14,11 @@
 //    operand registers through a ring of PF k steps (the packed tile layout:
 //    one contiguous kilobyte per wavefront load; the canonical layout works
 //    too, with 64-byte row pieces).
-//  - MXFP8 (k_expert_gemm_big): waves form 2 (rows) x 4 (weight rows), each
-//    a 64 x 64 block; the gate/up epilogue encodes h to MXFP8 directly.
-//  - NVFP4 (k_expert_gemm_big_nv): waves form 1 x 8, each all 128 rows x 32
-//    weight rows, so each weight fragment is expanded to f16 once per
-//    workgroup (see there).
+//  - Waves form 1 (rows) x 8 (weight rows): each wave owns all 128 rows x 32
+//    weight rows, so every weight fragment is loaded (and, for NVFP4,
+//    expanded to f16) by exactly one wave and feeds 8 MFMAs.
+//  - MXFP8 (k_expert_gemm_big_mx): the gate/up epilogue encodes h to MXFP8
+//    directly.  NVFP4 (k_expert_gemm_big_nv): see there.
 // Each weight element is fetched once per 128 rows of an expert; the
 // activation tile once per 256 weight rows.  Work items (row tile, weight
 // tile) are ordered so that the items one XCD runs back to back are
@@ -75,15 +75,19 @@ constexpr int abuf_bytes() {
 
 }  // namespace
 
+// MXFP8: each wave owns all 128 rows x 32 weight rows (8 x 2 scaled-MFMA
+// tiles), so every weight fragment is loaded by exactly one wave (with waves
+// as 2 row halves x 4, both halves would load it: 80 instead of 48 KB of
+// loads per workgroup and k step).  A wave's 16 h columns of a gate/up row
+// are half of an MX block; the block maximum is completed across the wave
+// pair through LDS.
 template <int STAGE, bool PACKED, int PF>
-__global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
+__global__ __launch_bounds__(512) void k_expert_gemm_big_mx(GemmArgs a) {
   static_assert(PF >= 1 && PF <= 3, "ring depth");
   constexpr int ABUF = abuf_bytes<2>();
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   __shared__ int tok[BM];
 
-  // XCD-aware order: work item L = (weight tile L / nt, row tile L % nt);
-  // consecutive items of one XCD are consecutive row tiles of one weight tile
   const int nt = a.ntiles[0], nx = STAGE == 0 ? a.F / 128 : a.H / BNW;
   const int items = nx * nt;
   const int hw = blockIdx.x;
@@ -96,7 +100,6 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   const int rows = min(BM, a.offsets[el + 1] - row0);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave & 1, wn = wave >> 1;
   const int r = lane & 15, g = lane >> 4;
   const int K = STAGE == 0 ? a.H : a.F;
   const int NS = K / 128;
@@ -108,99 +111,85 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   if (tid < BM) tok[tid] = tid < rows ? (STAGE == 0 ? a.sorted[row0 + tid] / a.k : row0 + tid) : -1;
   __syncthreads();
 
-  // ---- activation staging ------------------------------------------------
-  // Wave w stages row tile w: lane l takes row 16 w + l%16 and quarter
-  // aq = l/16 of the k step, so each LDS store of the wave is 1 KB contiguous
-  // (bank-conflict free).
-  const int ar = 16 * wave + (lane & 15), aq = lane >> 4;
-  const int at = tok[ar] >= 0 ? tok[ar] : tok[0];     // rows past the tile: outputs discarded
-  const uint8_t* acode = a.a_codes + (size_t)at * row_bytes;
-  const uint8_t* asc = a.a_sc + (size_t)at * sc_bytes;
+  // activation staging: wave w stages row tile w, lane l row 16 w + l%16 and
+  // quarter aq = l/16 of the k step (32 bytes), so each LDS store of the
+  // wave is 1 KB contiguous (bank-conflict free)
+  const int ar = 16 * wave + r, aq = g;
+  const int at = tok[ar] >= 0 ? tok[ar] : tok[0];
+  const uint8_t* acode = a.a_codes + (size_t)at * row_bytes + 32 * aq;
+  const uint8_t* asc = a.a_sc + (size_t)at * sc_bytes + aq;
   auto aload = [&](int s, AStage8& st) {
-    const v4u* p = reinterpret_cast<const v4u*>(acode + s * 128 + 32 * aq);
+    const v4u* p = reinterpret_cast<const v4u*>(acode + s * 128);
     st.lo = p[0];
     st.hi = p[1];
-    st.sc = asc[s * 4 + aq];
+    st.sc = asc[s * 4];
   };
   auto astore = [&](int buf, const AStage8& st) {
-    uint8_t* A = lds + buf * ABUF;
-    const int f = ar >> 4, rr = ar & 15;
-    // bytes [32 aq, +32) of the row's step are column groups 2(aq%2) and
-    // 2(aq%2)+1: their first halves for aq < 2, second halves for aq >= 2
     const int h = aq >> 1, g0 = 2 * (aq & 1);
-    uint8_t* T = A + f * 2112;
-    *reinterpret_cast<v4u*>(T + 1024 * h + (rr + 16 * g0) * 16) = st.lo;
-    *reinterpret_cast<v4u*>(T + 1024 * h + (rr + 16 * (g0 + 1)) * 16) = st.hi;
-    T[2048 + rr + 16 * aq] = (uint8_t)st.sc;
+    uint8_t* T = lds + buf * ABUF + wave * 2112;
+    *reinterpret_cast<v4u*>(T + 1024 * h + (r + 16 * g0) * 16) = st.lo;
+    *reinterpret_cast<v4u*>(T + 1024 * h + (r + 16 * (g0 + 1)) * 16) = st.hi;
+    T[2048 + r + 16 * aq] = (uint8_t)st.sc;
   };
 
-  // ---- weight fragments of this wave (4 column groups of 16 weight rows) ---
-  const uint8_t* brow[4];
-  const uint8_t* bsrow[4];
+  // this wave's two column groups: gate/up: the gate group and its up group
+  // (h columns bx*128 + 16 w ..); down: weight rows bx*256 + 32 w + 16 c
+  const uint8_t* brow[2];
+  const uint8_t* bsrow[2];
 #pragma unroll
-  for (int c = 0; c < 4; c++) {
-    int n0;   // first weight row of column group c
-    if (STAGE == 0)   // c = 0,1: gate rows; c = 2,3: the matching up rows
-      n0 = (c < 2 ? 0 : a.F) + bx * 128 + 32 * wn + 16 * (c & 1);
-    else
-      n0 = bx * BNW + 64 * wn + 16 * c;
+  for (int c = 0; c < 2; c++) {
+    const int n0 = STAGE == 0 ? c * a.F + bx * 128 + 16 * wave : bx * BNW + 32 * wave + 16 * c;
     if (PACKED) {
       const size_t t0 = (size_t)(n0 / 16) * NS;
-      brow[c] = wexp + t0 * 2048;
-      bsrow[c] = wsexp + t0 * 64;
+      brow[c] = wexp + t0 * 2048 + 16 * lane;
+      bsrow[c] = wsexp + t0 * 64 + lane;
     } else {
-      brow[c] = wexp + (size_t)(n0 + r) * row_bytes;
-      bsrow[c] = wsexp + (size_t)(n0 + r) * sc_bytes;
+      brow[c] = wexp + (size_t)(n0 + r) * row_bytes + 16 * g;
+      bsrow[c] = wsexp + (size_t)(n0 + r) * sc_bytes + g;
     }
   }
   auto bload = [&](int s, BFrag8* B) {
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
+    for (int c = 0; c < 2; c++) {
       if (PACKED) {
-        const uint8_t* t = brow[c] + (size_t)s * 2048 + 16 * lane;
+        const uint8_t* t = brow[c] + (size_t)s * 2048;
         B[c].lo = *reinterpret_cast<const v4u*>(t);
         B[c].hi = *reinterpret_cast<const v4u*>(t + 1024);
-        B[c].sc = bsrow[c][s * 64 + lane];
+        B[c].sc = bsrow[c][s * 64];
       } else {
-        B[c].lo = *reinterpret_cast<const v4u*>(brow[c] + s * 128 + 16 * g);
-        B[c].hi = *reinterpret_cast<const v4u*>(brow[c] + s * 128 + 64 + 16 * g);
-        B[c].sc = bsrow[c][s * 4 + g];
+        B[c].lo = *reinterpret_cast<const v4u*>(brow[c] + s * 128);
+        B[c].hi = *reinterpret_cast<const v4u*>(brow[c] + s * 128 + 64);
+        B[c].sc = bsrow[c][s * 4];
       }
     }
   };
 
-  v4f acc[4][4];
+  v4f acc[8][2];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int c = 0; c < 4; c++) acc[i][c] = v4f{0, 0, 0, 0};
+  for (int i = 0; i < 8; i++) acc[i][0] = acc[i][1] = v4f{0, 0, 0, 0};
 
   auto compute = [&](int buf, const BFrag8* B) {
     const uint8_t* A = lds + buf * ABUF;
-    v8i bv[4];
+    v8i bv[2];
 #pragma unroll
-    for (int c = 0; c < 4; c++)
+    for (int c = 0; c < 2; c++)
       bv[c] = v8i{(int)B[c].lo.x, (int)B[c].lo.y, (int)B[c].lo.z, (int)B[c].lo.w,
                   (int)B[c].hi.x, (int)B[c].hi.y, (int)B[c].hi.z, (int)B[c].hi.w};
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const uint8_t* T = A + (4 * wm + i) * 2112;
+    for (int i = 0; i < 8; i++) {
+      const uint8_t* T = A + i * 2112;
       const v4u lo = *reinterpret_cast<const v4u*>(T + 16 * lane);
       const v4u hi = *reinterpret_cast<const v4u*>(T + 1024 + 16 * lane);
       const v8i av = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       const int as = T[2048 + lane];
 #pragma unroll
-      for (int c = 0; c < 4; c++)
+      for (int c = 0; c < 2; c++)
         acc[i][c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv[c], acc[i][c], 0, 0, 0, as, 0,
                                                                      (int)B[c].sc);
     }
   };
 
-  // ---- main loop: PF steps of weights and activations in flight ----------
-  // NS is a multiple of PF; slot j holds the steps congruent to j mod PF.
-  // No load sits under a branch (see gemm.hip); past the end a step is
-  // re-read, harmlessly.
-  BFrag8 bring[PF][4];
+  BFrag8 bring[PF][2];
   AStage8 ast[PF];
 #pragma unroll
   for (int j = 0; j < PF; j++) {
@@ -210,14 +199,11 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
   astore(0, ast[0]);
   aload(min(PF, NS - 1), ast[0]);
   __syncthreads();
-  // ring slots are compile-time constants (a runtime slot index would put
-  // the staging registers in scratch memory)
   auto one_step = [&](auto J, int s0) {
     constexpr int j = decltype(J)::value;
     const int step = s0 + j;
     compute(step & 1, bring[j]);
     bload(min(step + PF, NS - 1), bring[j]);
-    // the next step's activations sit in slot (j+1)%PF; refill it after
     astore((step + 1) & 1, ast[(j + 1) % PF]);
     aload(min(step + 1 + PF, NS - 1), ast[(j + 1) % PF]);
     __syncthreads();
@@ -228,46 +214,47 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
     if constexpr (PF > 2) one_step(std::integral_constant<int, 2>{}, s0);
   }
 
-  // ---- epilogue straight from registers -----------------------------------
-  // acc reg q of lane l in tile (i, c): row 64 wm + 16 i + 4 (l/16) + q,
-  // weight row (column) 16 * (group c) + l%16.
+  // epilogue: acc reg q of lane l in tile (i, c): row 16 i + 4 (l/16) + q,
+  // weight row 16 * (group c) + l%16.  The main loop ended with a barrier,
+  // so the LDS buffers are free for the block maxima.
   const int cl = lane & 15, g4 = lane >> 4;
   if (STAGE == 0) {
     const float inv_c = 1.0f / a.cap;
+    float* amx = reinterpret_cast<float*>(lds);   // [128 rows][8 waves]
+    float h[8][4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 8; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const int m = 64 * wm + 16 * i + 4 * g4 + q;
-        const bool live = m < rows;
-        float h[2];
-#pragma unroll
-        for (int c = 0; c < 2; c++) h[c] = cap_swiglu(acc[i][c][q], acc[i][c + 2][q], a.cap_form, a.cap, inv_c);
-        // the wave's 32 columns of row m (16 lanes x 2 groups) are one MX
-        // block: amax across the 16 lanes of this row, then each lane
-        // encodes its two values; all lanes take part in the exchange
-        const int col0 = bx * 128 + 32 * wn;
-        float am = live ? fmaxf(fabsf(h[0]), fabsf(h[1])) : 0.0f;
+        const int m = 16 * i + 4 * g4 + q;
+        h[i][q] = cap_swiglu(acc[i][0][q], acc[i][1][q], a.cap_form, a.cap, inv_c);
+        float am = m < rows ? fabsf(h[i][q]) : 0.0f;
 #pragma unroll
         for (int o = 8; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, kWave));
+        if (cl == 0) amx[m * 8 + wave] = am;
+      }
+    __syncthreads();
+    const int col = bx * 128 + 16 * wave + cl;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int m = 16 * i + 4 * g4 + q;
+        if (m >= rows) continue;
+        const float am = fmaxf(amx[m * 8 + wave], amx[m * 8 + (wave ^ 1)]);
         const int E = mx_exponent(am);
-        const float step = pow2f(-E);
-        if (live) {
-          uint8_t* qrow = a.out_q + (size_t)(row0 + m) * a.F + col0;
-          qrow[cl] = (uint8_t)mx_encode(h[0], step);
-          qrow[16 + cl] = (uint8_t)mx_encode(h[1], step);
-          if (cl == 0) a.out_s[(size_t)(row0 + m) * (a.F / 32) + col0 / 32] = (uint8_t)(E + 127);
-        }
+        a.out_q[(size_t)(row0 + m) * a.F + col] = (uint8_t)mx_encode(h[i][q], pow2f(-E));
+        if (cl == 0 && (wave & 1) == 0) a.out_s[(size_t)(row0 + m) * (a.F / 32) + col / 32] = (uint8_t)(E + 127);
       }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 8; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const int m = 64 * wm + 16 * i + 4 * g4 + q;
+        const int m = 16 * i + 4 * g4 + q;
         if (m >= rows) continue;
 #pragma unroll
-        for (int c = 0; c < 4; c++) a.out[(size_t)(row0 + m) * a.H + bx * BNW + 64 * wn + 16 * c + cl] = acc[i][c][q];
+        for (int c = 0; c < 2; c++) a.out[(size_t)(row0 + m) * a.H + bx * BNW + 32 * wave + 16 * c + cl] = acc[i][c][q];
       }
   }
 }
@@ -281,7 +268,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big(GemmArgs a) {
 // expansion work per MFMA of the 2 x 4 arrangement, for twice the LDS reads
 // (about half of gfx950's LDS bandwidth at the MFMA rate).  The next part's
 // activation fragments are read from LDS while the current part's MFMAs run.
-template <bool PACKED, int STAGE, int PF>
+template <int STAGE, bool PACKED, int PF>
 __global__ __launch_bounds__(512) void k_expert_gemm_big_nv(GemmArgs a) {
   static_assert(PF >= 1 && PF <= 3, "ring depth");
   constexpr int ABUF = abuf_bytes<1>();
@@ -289,7 +276,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_nv(GemmArgs a) {
   __shared__ int tok[BM];
   __shared__ float rgs[BM];
 
-  // XCD-aware order as in k_expert_gemm_big
+  // XCD-aware order as in k_expert_gemm_big_mx
   const int nt = a.ntiles[0], nx = STAGE == 0 ? a.F / 128 : a.H / BNW;
   const int items = nx * nt;
   const int hw = blockIdx.x;
@@ -317,7 +304,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_nv(GemmArgs a) {
   }
   __syncthreads();
 
-  // activation staging exactly as in k_expert_gemm_big (wave w: row tile w;
+  // activation staging as in k_expert_gemm_big_mx (wave w: row tile w;
   // NVFP4 expanded to f16 on the way into LDS)
   const int ar = 16 * wave + r, aq = g;
   const int at = tok[ar] >= 0 ? tok[ar] : tok[0];
@@ -399,7 +386,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_nv(GemmArgs a) {
   };
 
   // main loop: PF steps of weights and activations in flight (as in
-  // k_expert_gemm_big; ring slots are compile-time constants)
+  // k_expert_gemm_big_mx; ring slots are compile-time constants)
   BFrag4 bring[PF][2];
   AStage4 ast[PF];
 #pragma unroll
@@ -464,7 +451,7 @@ namespace {
 template <int ST, bool PK, int PF>
 void launch_mx_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
   const size_t lds = 2 * abuf_bytes<2>();
-  hipLaunchKernelGGL((k_expert_gemm_big<ST, PK, PF>), grid, dim3(WAVES * 64), lds, stream, a);
+  hipLaunchKernelGGL((k_expert_gemm_big_mx<ST, PK, PF>), grid, dim3(WAVES * 64), lds, stream, a);
 }
 
 template <int ST, bool PK, int PF>
@@ -472,11 +459,11 @@ void launch_nv_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
   const size_t lds = 2 * abuf_bytes<1>();
   static bool done = false;   // dynamic LDS above 64 KiB must be allowed once
   if (!done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm_big_nv<PK, ST, PF>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm_big_nv<ST, PK, PF>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     done = true;
   }
-  hipLaunchKernelGGL((k_expert_gemm_big_nv<PK, ST, PF>), grid, dim3(WAVES * 64), lds, stream, a);
+  hipLaunchKernelGGL((k_expert_gemm_big_nv<ST, PK, PF>), grid, dim3(WAVES * 64), lds, stream, a);
 }
 
 template <int FMT, int ST, bool PK>
