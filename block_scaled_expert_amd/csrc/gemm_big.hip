@@ -473,7 +473,8 @@ void launch_pf(const GemmArgs& a, dim3 grid, hipStream_t stream) {
     if (ns % 2 == 0) launch_nv_one<ST, PK, 2>(a, grid, stream);
     else launch_nv_one<ST, PK, 1>(a, grid, stream);
   } else {
-    if (ns % 2 == 0) launch_mx_one<ST, PK, 2>(a, grid, stream);
+    if (ns % 3 == 0) launch_mx_one<ST, PK, 3>(a, grid, stream);
+    else if (ns % 2 == 0) launch_mx_one<ST, PK, 2>(a, grid, stream);
     else launch_mx_one<ST, PK, 1>(a, grid, stream);
   }
 }
