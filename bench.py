@@ -131,6 +131,56 @@ def cpu_baseline(w, x, wr, b, budget_s: float = 20.0):
                       f"{t_used:.1f} s of CPU work"}
 
 
+def encode_bench(args) -> int:
+    """Time the GPU weight encoder on n bf16 experts of the Inkling shape
+    (gate/up [n][2][2304][4608], down [n][4608][2304], values N(0, 0.02^2)).
+    A step encodes all of them.  Algorithmic bytes per element: 2 read
+    (bf16) plus the encoded bytes written (NVFP4 0.5625, MXFP8 1.03125)."""
+    import torch
+    import block_scaled_expert_amd as bse
+    fmt, n, H, Fd = args.encode, args.encode_experts, 4608, 2304
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    wg = (torch.randn((2 * n, Fd, H), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    wd = (torch.randn((n, H, Fd), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    nv = fmt == "nvfp4"
+    c13 = torch.empty((2 * n, Fd, H // 2 if nv else H), dtype=torch.uint8, device="cuda")
+    s13 = torch.empty((2 * n, Fd, H // (16 if nv else 32)), dtype=torch.uint8, device="cuda")
+    c2 = torch.empty((n, H, Fd // 2 if nv else Fd), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((n, H, Fd // (16 if nv else 32)), dtype=torch.uint8, device="cuda")
+    gs = torch.empty((n, 3), dtype=torch.float32, device="cuda") if nv else None
+    ws = torch.empty(2 * n, dtype=torch.int32, device="cuda") if nv else None
+
+    def step():
+        bse.encode_weights(fmt, wg, c13, s13, gs=gs, gs_group=2, gs_stride=3, ws=ws)
+        bse.encode_weights(fmt, wd, c2, s2, gs=gs.view(-1)[2:] if nv else None, gs_group=1, gs_stride=3, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    elems = 3.0 * n * Fd * H
+    alg = elems * (2 + (0.5 + 1 / 16 if nv else 1 + 1 / 32)) + (3 * n * 4 if nv else 0)
+    gbs = alg / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "expert weight encode throughput (bf16 -> checkpoint format, scales recomputed)",
+        "value": round(n / (ms * 1e-3), 1), "unit": "experts/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 in, " + fmt + " out", "data": "synthetic (N(0, 0.02^2) bf16)",
+        "config": {"workload": f"encode {n} experts, H4608, F2304", "experts": n, "format": fmt},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "per_launch": f"{int(elems)} elements x (2 B read + encoded bytes written)"},
+    }))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +194,9 @@ def main() -> int:
                     help="replay each step as a captured HIP graph (launch overhead removed)")
     ap.add_argument("--layout", choices=["packed", "canonical"], default="packed",
                     help="expert weight layout (packed: moe_prepare_weights at load time)")
+    ap.add_argument("--encode", choices=["nvfp4", "mxfp8"], default=None,
+                    help="instead of the layer: time moe_encode_weights on bf16 experts of the Inkling shape")
+    ap.add_argument("--encode-experts", type=int, default=64)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -158,6 +211,8 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration()
         return 0
+    if args.encode:
+        return encode_bench(args)
 
     w = synth.WORKLOADS[args.workload]
     T, H, E, k = w.tokens, w.hidden, w.experts, w.top_k

@@ -25,7 +25,8 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 STAGES = ("quant_x", "dispatch", "gate_up", "quant_h", "down", "combine")
 
 EXPORTED = ("moe_status_string", "moe_check_arch", "moe_validate_config", "moe_workspace_size",
-            "moe_quantize_act", "moe_route", "moe_dispatch", "moe_prepare_weights", "moe_forward")
+            "moe_quantize_act", "moe_route", "moe_dispatch", "moe_prepare_weights", "moe_forward",
+            "moe_encode_weights", "moe_decode_weights")
 LAYOUT_CANONICAL, LAYOUT_PACKED = 0, 1
 
 
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
     lib.moe_validate_config.argtypes = [ctypes.POINTER(CConfig)]
     lib.moe_workspace_size.argtypes = [ctypes.POINTER(CConfig), ctypes.POINTER(sz)]
     lib.moe_quantize_act.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp]
+    lib.moe_encode_weights.argtypes = [i32, i32, vp, i32, i32, i32, vp, vp, vp, i32, i32, vp, sz, vp]
+    lib.moe_decode_weights.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.moe_route.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_dispatch.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, vp, vp, sz, vp]
     lib.moe_prepare_weights.argtypes = [ctypes.POINTER(CConfig), ctypes.POINTER(CWeights), ctypes.POINTER(CWeights),
@@ -164,6 +167,55 @@ def quantize_act(fmt: str, x, codes, scales, row_gs=None) -> None:
             _ptr(scales, torch.uint8, (rows, cols // (16 if nv else 32)), "scales"),
             _ptr(row_gs, torch.float32, (rows,), "row_gs") if nv else None, _stream())
     _ok(load().moe_quantize_act(*args), "moe_quantize_act")
+
+
+def _check_gs(gs, nmat: int, group: int, stride: int) -> None:
+    if gs is None or group < 1 or stride < group:
+        raise ValueError("NVFP4 needs gs, gs_group >= 1 and gs_stride >= gs_group")
+    need = ((nmat - 1) // group) * stride + (nmat - 1) % group + 1 if nmat > 0 else 0
+    if gs.numel() < need:
+        raise ValueError(f"gs must hold at least {need} floats")
+
+
+def encode_weights(fmt: str, w, codes, scales, gs=None, gs_group: int = 1, gs_stride: int = 1,
+                   ws=None) -> None:
+    """Matrices w [nmat, rows, cols] (bf16 or fp32) to NVFP4 (one fp32 scale
+    per matrix, recomputed from its max |w|, written to gs[(m // gs_group) *
+    gs_stride + m % gs_group]; ws: int32 scratch of at least nmat elements)
+    or MXFP8.  codes / scales: uint8 [nmat, rows, cols/2 or cols] and
+    [nmat, rows, cols/16 or cols/32]."""
+    import torch
+    nmat, rows, cols = w.shape
+    dt = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}.get(w.dtype)
+    if dt is None:
+        raise ValueError("w must be bfloat16 or float32")
+    nv = fmt == "nvfp4"
+    _ptr(w, name="w")
+    if nv:
+        _check_gs(gs, nmat, gs_group, gs_stride)
+        if ws is None or ws.numel() < nmat:
+            raise ValueError(f"ws must hold at least {nmat} int32")
+    args = (FMTS[fmt], dt, _ptr(w), nmat, rows, cols,
+            _ptr(codes, torch.uint8, (nmat, rows, cols // 2 if nv else cols), "codes"),
+            _ptr(scales, torch.uint8, (nmat, rows, cols // (16 if nv else 32)), "scales"),
+            _ptr(gs, torch.float32, None, "gs") if nv else None, gs_group, gs_stride,
+            _ptr(ws, torch.int32, None, "ws") if nv else None,
+            (ws.numel() * 4) if (nv and ws is not None) else 0, _stream())
+    _ok(load().moe_encode_weights(*args), "moe_encode_weights")
+
+
+def decode_weights(fmt: str, codes, scales, out, gs=None, gs_group: int = 1, gs_stride: int = 1) -> None:
+    """The fp32 values [nmat, rows, cols] of encoded matrices (see encode_weights)."""
+    import torch
+    nmat, rows, cols = out.shape
+    nv = fmt == "nvfp4"
+    if nv:
+        _check_gs(gs, nmat, gs_group, gs_stride)
+    args = (FMTS[fmt], _ptr(codes, torch.uint8, (nmat, rows, cols // 2 if nv else cols), "codes"),
+            _ptr(scales, torch.uint8, (nmat, rows, cols // (16 if nv else 32)), "scales"),
+            _ptr(gs, torch.float32, None, "gs") if nv else None, gs_group, gs_stride, nmat, rows, cols,
+            _ptr(out, torch.float32, None, "out"), _stream())
+    _ok(load().moe_decode_weights(*args), "moe_decode_weights")
 
 
 def route(cfg: Config, x, w_router, bias, topk_ids, topk_w, near_tie, ws) -> None:

@@ -152,6 +152,48 @@ int moe_quantize_act(int32_t fmt, int32_t dtype, const void* x, int32_t rows, in
                       static_cast<hipStream_t>(stream)) == 0 ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
+static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int moe_encode_weights(int32_t fmt, int32_t dtype, const void* w, int32_t nmat, int32_t rows, int32_t cols,
+                       uint8_t* codes, uint8_t* scales, float* gs, int32_t gs_group, int32_t gs_stride,
+                       void* ws, size_t ws_bytes, void* stream) {
+  if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8) return MOE_ERR_UNSUPPORTED_FORMAT;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
+  if (nmat < 0 || rows <= 0 || cols <= 0 || cols % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if ((long)nmat * rows > (1L << 30) || (long)nmat * rows * cols > (1L << 40)) return MOE_ERR_INVALID_ARG;
+  if (nmat == 0) return MOE_OK;
+  if (w == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(codes, 16)) return MOE_ERR_INVALID_ARG;
+  if (fmt == MOE_FMT_NVFP4) {
+    if (gs == nullptr || gs_group < 1 || gs_stride < gs_group || ws == nullptr || !aligned(ws, 4))
+      return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < (size_t)nmat * 4) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
+  const int d = device_check();
+  if (d != MOE_OK) return d;
+  return launch_encode_weights(fmt, dtype, w, nmat, rows, cols, codes, scales, gs, gs_group, gs_stride,
+                               static_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream)) == 0
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+int moe_decode_weights(int32_t fmt, const uint8_t* codes, const uint8_t* scales, const float* gs,
+                       int32_t gs_group, int32_t gs_stride, int32_t nmat, int32_t rows, int32_t cols, float* out,
+                       void* stream) {
+  if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8) return MOE_ERR_UNSUPPORTED_FORMAT;
+  if (nmat < 0 || rows <= 0 || cols <= 0 || cols % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if ((long)nmat * rows > (1L << 30) || (long)nmat * rows * cols > (1L << 40)) return MOE_ERR_INVALID_ARG;
+  if (nmat == 0) return MOE_OK;
+  if (codes == nullptr || scales == nullptr || out == nullptr || !aligned(codes, 8)) return MOE_ERR_INVALID_ARG;
+  if (fmt == MOE_FMT_NVFP4 && (gs == nullptr || gs_group < 1 || gs_stride < gs_group)) return MOE_ERR_INVALID_ARG;
+  const int d = device_check();
+  if (d != MOE_OK) return d;
+  return launch_decode_weights(fmt, codes, scales, gs, nmat, rows, cols, gs_group, gs_stride, out,
+                               static_cast<hipStream_t>(stream)) == 0
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
 int moe_route(const moe_config* c, const void* x, int32_t T, const void* w_router, const float* bias,
               int32_t* topk_ids, float* topk_w, uint8_t* near_tie, void* ws, size_t ws_bytes,
               void* stream) {

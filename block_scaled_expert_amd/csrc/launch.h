@@ -45,6 +45,16 @@ int launch_prep_small(int fmt, const uint16_t* x, int T, int H, uint8_t* xq, uin
                       const int32_t* ids, int P, int E_begin, int E_local, int tile_m, const DispatchBufs& b,
                       hipStream_t stream);
 
+// Weight encoding: nmat matrices [rows][cols] (dtype 0 bf16, 1 fp32) to
+// canonical NVFP4 (fmt 1: one fp32 scale per matrix, written to
+// gs[(m / gs_group) * gs_stride + m % gs_group]; amax: nmat words of device
+// scratch) or MXFP8 (fmt 2), and back to fp32.
+int launch_encode_weights(int fmt, int dtype, const void* w, int nmat, int rows, int cols, uint8_t* codes,
+                          uint8_t* scales, float* gs, int gs_group, int gs_stride, uint32_t* amax,
+                          hipStream_t stream);
+int launch_decode_weights(int fmt, const uint8_t* codes, const uint8_t* scales, const float* gs, int nmat, int rows,
+                          int cols, int gs_group, int gs_stride, float* out, hipStream_t stream);
+
 struct GemmArgs {
   int fmt;                 // 1 NVFP4, 2 MXFP8
   int H, F, k;

@@ -172,6 +172,41 @@ int moe_workspace_size(const moe_config* cfg, size_t* bytes);
 int moe_quantize_act(int32_t fmt, int32_t dtype, const void* x, int32_t rows, int32_t cols,
                      uint8_t* codes, uint8_t* scales, float* row_gs, void* stream);
 
+/* moe_encode_weights: expert weight matrices to the checkpoint formats on
+ * the GPU, with every scale recomputed from the data -- what a weight sync
+ * does when it re-encodes updated experts (Miles docs "inkling-2-small",
+ * section 5; formats: SGLang cookbook "Inkling-2-Small", section 2
+ * "Checkpoints").
+ *  w: nmat matrices [nmat][rows][cols], bf16 (dtype MOE_DTYPE_BF16) or fp32,
+ *     16-byte aligned; cols a multiple of 32.  Values are assumed finite.
+ *  NVFP4: codes [nmat][rows][cols/2] (16-byte aligned), E4M3 block scales
+ *     [nmat][rows][cols/16]; one fp32 scale per matrix: A = max|w| over the
+ *     matrix, gs = A/2688 (1 if A == 0), then the blocks exactly as in
+ *     moe_quantize_act with that gs.  Matrix m's gs is written to
+ *     gs[(m / gs_group) * gs_stride + m % gs_group]: for the canonical
+ *     moe_expert_weights of n experts, encode the gate/up matrices as
+ *     [n][2][F][H] with gs_group 2, gs_stride 3 into gs, and the down
+ *     matrices [n][H][F] with gs_group 1, gs_stride 3 into gs + 2.
+ *     ws: device scratch of at least 4 * nmat bytes (caller-owned).
+ *  MXFP8: codes [nmat][rows][cols], E8M0 scales [nmat][rows][cols/32]
+ *     exactly as moe_quantize_act; gs, gs_group, gs_stride and ws unused.
+ * Asynchronous on `stream`; bit-identical to the definition.  Errors:
+ * MOE_ERR_UNSUPPORTED_FORMAT, MOE_ERR_INVALID_ARG (shape, alignment, null
+ * pointers), MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_UNSUPPORTED_DEVICE,
+ * MOE_ERR_LAUNCH. */
+int moe_encode_weights(int32_t fmt, int32_t dtype, const void* w, int32_t nmat, int32_t rows, int32_t cols,
+                       uint8_t* codes, uint8_t* scales, float* gs, int32_t gs_group, int32_t gs_stride,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* moe_decode_weights: the inverse view, to fp32 [nmat][rows][cols]: NVFP4
+ * element = (E2M1 value * E4M3 block scale) * gs (the first product exact,
+ * one fp32 rounding), MXFP8 element = E4M3 value * 2^(scale - 127) (one
+ * fp32 rounding; may overflow to inf above the fp32 range).  Layouts and gs
+ * addressing as in moe_encode_weights; codes 8-byte aligned. */
+int moe_decode_weights(int32_t fmt, const uint8_t* codes, const uint8_t* scales, const float* gs,
+                       int32_t gs_group, int32_t gs_stride, int32_t nmat, int32_t rows, int32_t cols, float* out,
+                       void* stream);
+
 /* Router (SGLang blog "Performance": sigmoid, bias and top-k in one step;
  * Miles docs section 1: sigmoid routing, top-8 of 384).
  *  x [T][H] bf16; w_router [E][H] bf16; bias [E] fp32.

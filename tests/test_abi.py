@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_route", "moe_quantize_act", "moe_forward", "moe_dispatch", "moe_prepare_weights",
-              "moe_workspace_size", "moe_status_string", "moe_check_arch", "moe_validate_config"):
+              "moe_workspace_size", "moe_status_string", "moe_check_arch", "moe_validate_config",
+              "moe_encode_weights", "moe_decode_weights"):
         assert n in names
 
 
@@ -118,3 +119,21 @@ def test_host_checks_before_device(lib):
     # weights: bad layout value / canonical source required
     w = bse.CWeights(1, 1, 1, 1, 1, 5)
     assert lib.moe_prepare_weights(ctypes.byref(cc), ctypes.byref(w), ctypes.byref(bse.CWeights()), None) == -1
+
+
+def test_encode_decode_host_checks(lib):
+    """Weight encoder / decoder argument errors come back without a GPU."""
+    p = ctypes.c_void_p(0x1000)
+    enc, dec = lib.moe_encode_weights, lib.moe_decode_weights
+    assert enc(3, 0, p, 2, 16, 64, p, p, p, 1, 1, p, 64, None) == -5        # format
+    assert enc(1, 2, p, 2, 16, 64, p, p, p, 1, 1, p, 64, None) == -1        # dtype
+    assert enc(1, 0, p, 2, 16, 48, p, p, p, 1, 1, p, 64, None) == -1        # cols % 32
+    assert enc(1, 0, p, 0, 16, 64, None, None, None, 1, 1, None, 0, None) == 0   # nothing to do
+    assert enc(1, 0, None, 2, 16, 64, p, p, p, 1, 1, p, 64, None) == -1     # null input
+    assert enc(1, 0, ctypes.c_void_p(0x1008), 2, 16, 64, p, p, p, 1, 1, p, 64, None) == -1   # alignment
+    assert enc(1, 0, p, 2, 16, 64, p, p, None, 1, 1, p, 64, None) == -1     # NVFP4 needs gs
+    assert enc(1, 0, p, 2, 16, 64, p, p, p, 2, 1, p, 64, None) == -1        # stride < group
+    assert enc(1, 0, p, 4, 16, 64, p, p, p, 1, 1, p, 15, None) == -3        # scratch for 4 maxima
+    assert dec(3, p, p, p, 1, 1, 2, 16, 64, p, None) == -5
+    assert dec(1, p, p, None, 1, 1, 2, 16, 64, p, None) == -1
+    assert dec(2, p, p, None, 1, 1, 0, 16, 64, p, None) == 0
