@@ -457,12 +457,10 @@ void launch_mx_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
 template <int ST, bool PK, int PF>
 void launch_nv_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
   const size_t lds = 2 * abuf_bytes<1>();
-  static bool done = false;   // dynamic LDS above 64 KiB must be allowed once
-  if (!done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm_big_nv<ST, PK, PF>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    done = true;
-  }
+  // dynamic LDS of 64 KiB and more must be allowed explicitly; set on every
+  // launch (a host-side call) so no state is shared across threads or devices
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm_big_nv<ST, PK, PF>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL((k_expert_gemm_big_nv<ST, PK, PF>), grid, dim3(WAVES * 64), lds, stream, a);
 }
 
