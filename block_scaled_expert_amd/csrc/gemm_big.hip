@@ -259,17 +259,18 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_mx(GemmArgs a) {
   }
 }
 
-// NVFP4 variant: the same tile (128 rows x 256 weight rows, 8 waves, k step
-// 128, activations expanded to f16 once per workgroup in LDS) but the waves
-// form 1 (rows) x 8 (weight rows): each wave owns all 128 rows x 32 weight
-// rows (8 x 2 MFMA tiles).  The exact NVFP4 path is limited by vector-ALU
-// issue (operand expansion shares issue slots with the MFMAs); here every
-// weight fragment is expanded once per workgroup and feeds 8 MFMAs, half the
-// expansion work per MFMA of the 2 x 4 arrangement, for twice the LDS reads
-// (about half of gfx950's LDS bandwidth at the MFMA rate).  The next part's
-// activation fragments are read from LDS while the current part's MFMAs run.
+// NVFP4: the same tile (128 rows x 256 weight rows, 8 waves, k step 128,
+// activations expanded to f16 once per workgroup in LDS), waves 1 (rows) x 8
+// (weight rows): each wave owns all 128 rows x 32 weight rows (8 x 2 MFMA
+// tiles).  The exact NVFP4 path is limited by vector-ALU issue (operand
+// expansion shares issue slots with the MFMAs); here every weight fragment is
+// expanded once per workgroup and feeds 8 MFMAs, for twice the LDS reads of a
+// 2 x 4 arrangement (about half of gfx950's LDS bandwidth at the MFMA rate).
+// One step of weights in flight and a scheduling barrier between the four
+// 32-wide parts of a step keep the kernel within 128 registers, so two
+// workgroups (16 waves) share a CU and cover each other's latency.
 template <int STAGE, bool PACKED, int PF>
-__global__ __launch_bounds__(512) void k_expert_gemm_big_nv(GemmArgs a) {
+__global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
   static_assert(PF >= 1 && PF <= 3, "ring depth");
   constexpr int ABUF = abuf_bytes<1>();
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -361,27 +362,22 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_nv(GemmArgs a) {
       bs[c][0] = v2h{sp[0], sp[0]};
       bs[c][1] = v2h{sp[1], sp[1]};
     }
-    v8h av[2][8];
-#pragma unroll
-    for (int i = 0; i < 8; i++) av[0][i] = *reinterpret_cast<const v8h*>(A + i * 4096 + lane * 16);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      if (j < 3) {
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-          av[(j + 1) & 1][i] = *reinterpret_cast<const v8h*>(A + i * 4096 + (j + 1) * 1024 + lane * 16);
-      }
+      __builtin_amdgcn_sched_barrier(0);
       v8h bv[2];
 #pragma unroll
       for (int c = 0; c < 2; c++) {
         const uint32_t w = j == 0 ? B[c].q.x : j == 1 ? B[c].q.y : j == 2 ? B[c].q.z : B[c].q.w;
-        bv[c] = dq8(w, bs[c][j >> 1]);
+        bv[c] = dq8(w, j < 2 ? bs[c][0] : bs[c][1]);
       }
 #pragma unroll
-      for (int i = 0; i < 8; i++)
+      for (int i = 0; i < 8; i++) {
+        const v8h av = *reinterpret_cast<const v8h*>(A + i * 4096 + j * 1024 + lane * 16);
 #pragma unroll
         for (int c = 0; c < 2; c++)
-          acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[j & 1][i], bv[c], acc[i][c], 0, 0, 0);
+          acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[c], acc[i][c], 0, 0, 0);
+      }
     }
   };
 
@@ -466,18 +462,12 @@ void launch_nv_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
 
 template <int FMT, int ST, bool PK>
 void launch_pf(const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  const int ns = (ST == 0 ? a.H : a.F) / 128;
-  if constexpr (FMT == 1) {
-    if (ns % 2 == 0) launch_nv_one<ST, PK, 2>(a, grid, stream);
-    else launch_nv_one<ST, PK, 1>(a, grid, stream);
-  } else {
-    // one step of weights in flight per wave: the kernel then fits 128
-    // registers, so two workgroups (16 waves) share a CU and hide each
-    // other's latency -- faster than deeper rings at one workgroup per CU
-    // (EP share gate/up 258 -> 222 us, same box)
-    (void)ns;
-    launch_mx_one<ST, PK, 1>(a, grid, stream);
-  }
+  // One step of weights in flight per wave: both kernels then fit 128
+  // registers, so two workgroups (16 waves) share a CU and hide each other's
+  // latency -- faster than deeper rings at one workgroup per CU (same-box
+  // A/B: EP share gate/up 258 -> 222 us, prefill gate/up 6.32 -> 5.77 ms).
+  if constexpr (FMT == 1) launch_nv_one<ST, PK, 1>(a, grid, stream);
+  else launch_mx_one<ST, PK, 1>(a, grid, stream);
 }
 
 }  // namespace
