@@ -61,10 +61,10 @@ Layout layout(const moe_config* c, int T) {
   L.pos = take(P * 4);
   L.work = take((size_t)L.max_tiles * 2 * 4);
   L.ntiles = take(4);
-  L.h = take(P * F * 4);
+  L.h = take(nv ? P * F * 4 : 0);    // fp32 h: NVFP4 only (MXFP8 h is encoded by the gate/up epilogue)
   L.hq = take(P * (nv ? F / 2 : F));
   L.hs = take(P * (nv ? F / 16 : F / 32));
-  L.hg = take(P * 4);
+  L.hg = take(nv ? P * 4 : 0);
   L.y = take(P * H * 4);
   L.total = o;
   return L;
@@ -222,7 +222,7 @@ int moe_dispatch(const moe_config* c, const int32_t* topk_ids, int32_t T, int32_
   if ((st = check_ws(c, T, ws, ws_bytes)) != MOE_OK) return st;
   if ((st = device_check()) != MOE_OK) return st;
   const Layout L = layout(c, c->max_tokens);
-  DispatchBufs b;
+  DispatchBufs b{};
   b.counts = at<int32_t>(ws, L.counts);
   b.offsets = expert_offsets;
   b.sorted = sorted_pairs;
@@ -283,7 +283,7 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
 
   int tile_m = gemm_tile_m(T, k, c->num_experts);
   if (tile_m == 128 && !gemm_big_supported(H, F)) tile_m = 64;
-  DispatchBufs b;
+  DispatchBufs b{};
   b.counts = at<int32_t>(ws, L.counts);
   b.offsets = at<int32_t>(ws, L.offsets);
   b.sorted = at<int32_t>(ws, L.sorted);
@@ -313,7 +313,7 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   }
 
   // 3. gate/up GEMM + capped SwiGLU -> h (fp32, sorted rows)
-  GemmArgs g;
+  GemmArgs g{};
   g.fmt = c->fmt;
   g.H = H;
   g.F = F;
@@ -334,8 +334,8 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   g.tile_m = tile_m;
   g.cap_form = c->cap_form;
   g.cap = c->cap_form == MOE_CAP_NONE ? 1.0f : c->cap;
-  g.out = at<float>(ws, L.h);
   const bool fuse_h = c->fmt == MOE_FMT_MXFP8;   // MXFP8 h is encoded by the gate/up epilogue
+  g.out = fuse_h ? nullptr : at<float>(ws, L.h);
   g.out_q = fuse_h ? at<uint8_t>(ws, L.hq) : nullptr;
   g.out_s = fuse_h ? at<uint8_t>(ws, L.hs) : nullptr;
   record(events, 2 * MOE_STAGE_GATE_UP, s);
@@ -354,7 +354,7 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   GemmArgs d = g;
   d.a_codes = at<uint8_t>(ws, L.hq);
   d.a_sc = at<uint8_t>(ws, L.hs);
-  d.a_gs = at<float>(ws, L.hg);
+  d.a_gs = fuse_h ? nullptr : at<float>(ws, L.hg);
   d.w_codes = w->w2;
   d.w_sc = w->w2_sc;
   d.out = at<float>(ws, L.y);
