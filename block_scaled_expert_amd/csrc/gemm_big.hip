@@ -72,32 +72,53 @@ template <int FMT>
 constexpr int abuf_bytes() {
   return FMT == 1 ? 8 * 4096 : 8 * (2048 + 64);
 }
+// LDS bytes ahead of the activation buffers: the tile rows' token indices
+// and (NVFP4) their activation scales.
+constexpr int kBigHead = 2 * 4 * BM;
 
 }  // namespace
 
-// MXFP8: each wave owns all 128 rows x 32 weight rows (8 x 2 scaled-MFMA
-// tiles), so every weight fragment is loaded by exactly one wave (with waves
-// as 2 row halves x 4, both halves would load it: 80 instead of 48 KB of
-// loads per workgroup and k step).  A wave's 16 h columns of a gate/up row
-// are half of an MX block; the block maximum is completed across the wave
-// pair through LDS.
-template <int STAGE, bool PACKED, int PF>
-__global__ __launch_bounds__(512) void k_expert_gemm_big_mx(GemmArgs a) {
-  static_assert(PF >= 1 && PF <= 3, "ring depth");
-  constexpr int ABUF = abuf_bytes<2>();
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int tok[BM];
-
-  const int nt = a.ntiles[0], nx = STAGE == 0 ? a.F / 128 : a.H / BNW;
+// A work item of a large-M launch: one row tile of an expert (a dispatch
+// work-list entry) and one weight tile.  Work items are ordered so that the
+// items one XCD runs back to back are consecutive row tiles of the same
+// weight tile.  Returns false for workgroups beyond the launch's items.
+struct BigItem {
+  int el, row0, rows, bx;
+};
+__device__ inline bool big_item(const GemmArgs& a, int stage, BigItem& it) {
+  const int nt = a.ntiles[0], nx = stage == 0 ? a.F / 128 : a.H / BNW;
   const int items = nx * nt;
   const int hw = blockIdx.x;
-  if (hw >= items) return;
+  if (hw >= items) return false;
   const int q8 = items / 8, r8 = items % 8, xcd = hw % 8;
   const int L = xcd * q8 + min(xcd, r8) + hw / 8;
-  const int tile = L % nt, bx = L / nt;
-  const int el = a.worklist[2 * tile], m0 = a.worklist[2 * tile + 1];
-  const int row0 = a.offsets[el] + m0;
-  const int rows = min(BM, a.offsets[el + 1] - row0);
+  const int tile = L % nt;
+  it.bx = L / nt;
+  it.el = a.worklist[2 * tile];
+  it.row0 = a.offsets[it.el] + a.worklist[2 * tile + 1];
+  it.rows = min(BM, a.offsets[it.el + 1] - it.row0);
+  return true;
+}
+
+// 16-row sub-tiles that hold rows of the item (an expert's last row tile is
+// usually partial); the tile bodies are compiled per count, so a partial
+// tile issues neither the loads, the LDS traffic nor the MFMAs of its empty
+// sub-tiles.
+__device__ inline int big_subtiles(int rows) { return min(8, max(1, (rows + 15) >> 4)); }
+
+// MXFP8: each wave owns all of the tile's rows x 32 weight rows (up to 8 x 2
+// scaled-MFMA tiles), so every weight fragment is loaded by exactly one wave
+// (with waves as 2 row halves x 4, both halves would load it: 80 instead of
+// 48 KB of loads per workgroup and k step).  A wave's 16 h columns of a
+// gate/up row are half of an MX block; the block maximum is completed across
+// the wave pair through LDS.  Token indices of the tile's rows are in the
+// first 512 bytes of `lds`, the activation buffers follow.
+template <int STAGE, bool PACKED, int PF, int NSUB>
+__device__ __forceinline__ void big_mx_tile(const GemmArgs& a, const BigItem& it, uint8_t* lds) {
+  constexpr int ABUF = abuf_bytes<2>();
+  const int* tok = reinterpret_cast<const int*>(lds);
+  uint8_t* abuf = lds + kBigHead;
+  const int el = it.el, row0 = it.row0, rows = it.rows, bx = it.bx;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
@@ -108,12 +129,11 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_mx(GemmArgs a) {
   const uint8_t* wexp = a.w_codes + (size_t)el * NW * row_bytes;
   const uint8_t* wsexp = a.w_sc + (size_t)el * NW * sc_bytes;
 
-  if (tid < BM) tok[tid] = tid < rows ? (STAGE == 0 ? a.sorted[row0 + tid] / a.k : row0 + tid) : -1;
-  __syncthreads();
-
   // activation staging: wave w stages row tile w, lane l row 16 w + l%16 and
-  // quarter aq = l/16 of the k step (32 bytes), so each LDS store of the
-  // wave is 1 KB contiguous (bank-conflict free)
+  // quarter aq = l/16 of the k step (32 bytes), so each LDS store of the wave
+  // is 1 KB contiguous (bank-conflict free).  Waves past the tile's rows
+  // stage copies of its first row (a branch here costs the partial-tile
+  // bodies their registers).
   const int ar = 16 * wave + r, aq = g;
   const int at = tok[ar] >= 0 ? tok[ar] : tok[0];
   const uint8_t* acode = a.a_codes + (size_t)at * row_bytes + 32 * aq;
@@ -126,7 +146,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_mx(GemmArgs a) {
   };
   auto astore = [&](int buf, const AStage8& st) {
     const int h = aq >> 1, g0 = 2 * (aq & 1);
-    uint8_t* T = lds + buf * ABUF + wave * 2112;
+    uint8_t* T = abuf + buf * ABUF + wave * 2112;
     *reinterpret_cast<v4u*>(T + 1024 * h + (r + 16 * g0) * 16) = st.lo;
     *reinterpret_cast<v4u*>(T + 1024 * h + (r + 16 * (g0 + 1)) * 16) = st.hi;
     T[2048 + r + 16 * aq] = (uint8_t)st.sc;
@@ -164,19 +184,19 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_mx(GemmArgs a) {
     }
   };
 
-  v4f acc[8][2];
+  v4f acc[NSUB][2];
 #pragma unroll
-  for (int i = 0; i < 8; i++) acc[i][0] = acc[i][1] = v4f{0, 0, 0, 0};
+  for (int i = 0; i < NSUB; i++) acc[i][0] = acc[i][1] = v4f{0, 0, 0, 0};
 
   auto compute = [&](int buf, const BFrag8* B) {
-    const uint8_t* A = lds + buf * ABUF;
+    const uint8_t* A = abuf + buf * ABUF;
     v8i bv[2];
 #pragma unroll
     for (int c = 0; c < 2; c++)
       bv[c] = v8i{(int)B[c].lo.x, (int)B[c].lo.y, (int)B[c].lo.z, (int)B[c].lo.w,
                   (int)B[c].hi.x, (int)B[c].hi.y, (int)B[c].hi.z, (int)B[c].hi.w};
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
+    for (int i = 0; i < NSUB; i++) {
       const uint8_t* T = A + i * 2112;
       const v4u lo = *reinterpret_cast<const v4u*>(T + 16 * lane);
       const v4u hi = *reinterpret_cast<const v4u*>(T + 1024 + 16 * lane);
@@ -216,14 +236,14 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_mx(GemmArgs a) {
 
   // epilogue: acc reg q of lane l in tile (i, c): row 16 i + 4 (l/16) + q,
   // weight row 16 * (group c) + l%16.  The main loop ended with a barrier,
-  // so the LDS buffers are free for the block maxima.
+  // so the activation buffers are free for the block maxima.
   const int cl = lane & 15, g4 = lane >> 4;
   if (STAGE == 0) {
     const float inv_c = 1.0f / a.cap;
-    float* amx = reinterpret_cast<float*>(lds);   // [128 rows][8 waves]
-    float h[8][4];
+    float* amx = reinterpret_cast<float*>(abuf);   // [128 rows][8 waves]
+    float h[NSUB][4];
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < NSUB; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 16 * i + 4 * g4 + q;
@@ -236,7 +256,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_mx(GemmArgs a) {
     __syncthreads();
     const int col = bx * 128 + 16 * wave + cl;
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < NSUB; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 16 * i + 4 * g4 + q;
@@ -248,7 +268,7 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_mx(GemmArgs a) {
       }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < NSUB; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 16 * i + 4 * g4 + q;
@@ -259,35 +279,48 @@ __global__ __launch_bounds__(512) void k_expert_gemm_big_mx(GemmArgs a) {
   }
 }
 
+template <int STAGE, bool PACKED, int PF>
+__global__ __launch_bounds__(512, 4) void k_expert_gemm_big_mx(GemmArgs a) {
+  static_assert(PF >= 1 && PF <= 3, "ring depth");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  BigItem it;
+  if (!big_item(a, STAGE, it)) return;
+  const int tid = threadIdx.x;
+  if (tid < BM)
+    reinterpret_cast<int*>(lds)[tid] =
+        tid < it.rows ? (STAGE == 0 ? a.sorted[it.row0 + tid] / a.k : it.row0 + tid) : -1;
+  __syncthreads();
+  // 6 or 7 sub-tiles run the full body: the compiler's schedules for those
+  // two counts need more than 128 registers
+  switch (big_subtiles(it.rows)) {
+    case 1: big_mx_tile<STAGE, PACKED, PF, 1>(a, it, lds); break;
+    case 2: big_mx_tile<STAGE, PACKED, PF, 2>(a, it, lds); break;
+    case 3: big_mx_tile<STAGE, PACKED, PF, 3>(a, it, lds); break;
+    case 4: big_mx_tile<STAGE, PACKED, PF, 4>(a, it, lds); break;
+    case 5: big_mx_tile<STAGE, PACKED, PF, 5>(a, it, lds); break;
+    default: big_mx_tile<STAGE, PACKED, PF, 8>(a, it, lds); break;
+  }
+}
+
 // NVFP4: the same tile (128 rows x 256 weight rows, 8 waves, k step 128,
 // activations expanded to f16 once per workgroup in LDS), waves 1 (rows) x 8
-// (weight rows): each wave owns all 128 rows x 32 weight rows (8 x 2 MFMA
-// tiles).  The exact NVFP4 path is limited by vector-ALU issue (operand
-// expansion shares issue slots with the MFMAs); here every weight fragment is
-// expanded once per workgroup and feeds 8 MFMAs, for twice the LDS reads of a
-// 2 x 4 arrangement (about half of gfx950's LDS bandwidth at the MFMA rate).
-// One step of weights in flight and a scheduling barrier between the four
-// 32-wide parts of a step keep the kernel within 128 registers, so two
-// workgroups (16 waves) share a CU and cover each other's latency.
-template <int STAGE, bool PACKED, int PF>
-__global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
-  static_assert(PF >= 1 && PF <= 3, "ring depth");
+// (weight rows): each wave owns all of the tile's rows x 32 weight rows (up
+// to 8 x 2 MFMA tiles).  The exact NVFP4 path is limited by vector-ALU issue
+// (operand expansion shares issue slots with the MFMAs); here every weight
+// fragment is expanded once per workgroup and feeds up to 8 MFMAs, for twice
+// the LDS reads of a 2 x 4 arrangement (about half of gfx950's LDS bandwidth
+// at the MFMA rate).  One step of weights in flight and a scheduling barrier
+// between the four 32-wide parts of a step keep the kernel within 128
+// registers, so two workgroups (16 waves) share a CU and cover each other's
+// latency.  `lds` starts with the rows' token indices (512 bytes) and
+// activation scales (512 bytes); the activation buffers follow.
+template <int STAGE, bool PACKED, int PF, int NSUB>
+__device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it, uint8_t* lds) {
   constexpr int ABUF = abuf_bytes<1>();
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  __shared__ int tok[BM];
-  __shared__ float rgs[BM];
-
-  // XCD-aware order as in k_expert_gemm_big_mx
-  const int nt = a.ntiles[0], nx = STAGE == 0 ? a.F / 128 : a.H / BNW;
-  const int items = nx * nt;
-  const int hw = blockIdx.x;
-  if (hw >= items) return;
-  const int q8 = items / 8, r8 = items % 8, xcd = hw % 8;
-  const int L = xcd * q8 + min(xcd, r8) + hw / 8;
-  const int tile = L % nt, bx = L / nt;
-  const int el = a.worklist[2 * tile], m0 = a.worklist[2 * tile + 1];
-  const int row0 = a.offsets[el] + m0;
-  const int rows = min(BM, a.offsets[el + 1] - row0);
+  const int* tok = reinterpret_cast<const int*>(lds);
+  const float* rgs = reinterpret_cast<const float*>(lds + 4 * BM);
+  uint8_t* abuf = lds + kBigHead;
+  const int el = it.el, row0 = it.row0, rows = it.rows, bx = it.bx;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
@@ -298,27 +331,23 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
   const uint8_t* wexp = a.w_codes + (size_t)el * NW * row_bytes;
   const uint8_t* wsexp = a.w_sc + (size_t)el * NW * sc_bytes;
 
-  if (tid < BM) {
-    const int tk = tid < rows ? (STAGE == 0 ? a.sorted[row0 + tid] / a.k : row0 + tid) : -1;
-    tok[tid] = tk;
-    rgs[tid] = tk >= 0 ? a.a_gs[tk] : 0.0f;
-  }
-  __syncthreads();
-
-  // activation staging as in k_expert_gemm_big_mx (wave w: row tile w;
-  // NVFP4 expanded to f16 on the way into LDS)
+  // activation staging as in big_mx_tile (wave w < NSUB: row tile w; NVFP4
+  // expanded to f16 on the way into LDS)
+  const bool stager = NSUB == 8 || wave < NSUB;
   const int ar = 16 * wave + r, aq = g;
   const int at = tok[ar] >= 0 ? tok[ar] : tok[0];
   const uint8_t* acode = a.a_codes + (size_t)at * row_bytes + 16 * aq;
   const uint8_t* asc = a.a_sc + (size_t)at * sc_bytes + 2 * aq;
   auto aload = [&](int s, AStage4& st) {
+    if (!stager) return;
     st.q = *reinterpret_cast<const v4u*>(acode + s * 64);
     st.sc = *reinterpret_cast<const uint16_t*>(asc + s * 8);
   };
   auto astore = [&](int buf, const AStage4& st) {
+    if (!stager) return;
     const v2h sp = sig2_of(st.sc);
     const v2h s0 = v2h{sp[0], sp[0]}, s1 = v2h{sp[1], sp[1]};
-    uint8_t* base = lds + buf * ABUF + wave * 4096 + lane * 16;
+    uint8_t* base = abuf + buf * ABUF + wave * 4096 + lane * 16;
     *reinterpret_cast<v8h*>(base + 0 * 1024) = dq8(st.q.x, s0);
     *reinterpret_cast<v8h*>(base + 1 * 1024) = dq8(st.q.y, s0);
     *reinterpret_cast<v8h*>(base + 2 * 1024) = dq8(st.q.z, s1);
@@ -349,12 +378,12 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
     }
   };
 
-  v4f acc[8][2];
+  v4f acc[NSUB][2];
 #pragma unroll
-  for (int i = 0; i < 8; i++) acc[i][0] = acc[i][1] = v4f{0, 0, 0, 0};
+  for (int i = 0; i < NSUB; i++) acc[i][0] = acc[i][1] = v4f{0, 0, 0, 0};
 
   auto compute = [&](int buf, const BFrag4* B) {
-    const uint8_t* A = lds + buf * ABUF;
+    const uint8_t* A = abuf + buf * ABUF;
     v2h bs[2][2];
 #pragma unroll
     for (int c = 0; c < 2; c++) {
@@ -372,7 +401,7 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
         bv[c] = dq8(w, j < 2 ? bs[c][0] : bs[c][1]);
       }
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
+      for (int i = 0; i < NSUB; i++) {
         const v8h av = *reinterpret_cast<const v8h*>(A + i * 4096 + j * 1024 + lane * 16);
 #pragma unroll
         for (int c = 0; c < 2; c++)
@@ -382,7 +411,7 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
   };
 
   // main loop: PF steps of weights and activations in flight (as in
-  // k_expert_gemm_big_mx; ring slots are compile-time constants)
+  // big_mx_tile; ring slots are compile-time constants)
   BFrag4 bring[PF][2];
   AStage4 ast[PF];
 #pragma unroll
@@ -416,7 +445,7 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
     const float wg = a.w_gs[3 * el + 0], wu = a.w_gs[3 * el + 1];
     const int col = bx * 128 + 16 * wave + cl;
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < NSUB; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 16 * i + 4 * g4 + q;
@@ -429,7 +458,7 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
   } else {
     const float wd = a.w_gs[3 * el + 2];
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < NSUB; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 16 * i + 4 * g4 + q;
@@ -442,17 +471,42 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
   }
 }
 
+template <int STAGE, bool PACKED, int PF>
+__global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
+  static_assert(PF >= 1 && PF <= 3, "ring depth");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  BigItem it;
+  if (!big_item(a, STAGE, it)) return;
+  const int tid = threadIdx.x;
+  if (tid < BM) {
+    const int tk = tid < it.rows ? (STAGE == 0 ? a.sorted[it.row0 + tid] / a.k : it.row0 + tid) : -1;
+    reinterpret_cast<int*>(lds)[tid] = tk;
+    reinterpret_cast<float*>(lds + 4 * BM)[tid] = tk >= 0 ? a.a_gs[tk] : 0.0f;
+  }
+  __syncthreads();
+  switch (big_subtiles(it.rows)) {
+    case 1: big_nv_tile<STAGE, PACKED, PF, 1>(a, it, lds); break;
+    case 2: big_nv_tile<STAGE, PACKED, PF, 2>(a, it, lds); break;
+    case 3: big_nv_tile<STAGE, PACKED, PF, 3>(a, it, lds); break;
+    case 4: big_nv_tile<STAGE, PACKED, PF, 4>(a, it, lds); break;
+    case 5: big_nv_tile<STAGE, PACKED, PF, 5>(a, it, lds); break;
+    case 6: big_nv_tile<STAGE, PACKED, PF, 6>(a, it, lds); break;
+    case 7: big_nv_tile<STAGE, PACKED, PF, 7>(a, it, lds); break;
+    default: big_nv_tile<STAGE, PACKED, PF, 8>(a, it, lds); break;
+  }
+}
+
 namespace {
 
 template <int ST, bool PK, int PF>
 void launch_mx_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  const size_t lds = 2 * abuf_bytes<2>();
+  const size_t lds = kBigHead + 2 * abuf_bytes<2>();
   hipLaunchKernelGGL((k_expert_gemm_big_mx<ST, PK, PF>), grid, dim3(WAVES * 64), lds, stream, a);
 }
 
 template <int ST, bool PK, int PF>
 void launch_nv_one(const GemmArgs& a, dim3 grid, hipStream_t stream) {
-  const size_t lds = 2 * abuf_bytes<1>();
+  const size_t lds = kBigHead + 2 * abuf_bytes<1>();
   // dynamic LDS of 64 KiB and more must be allowed explicitly; set on every
   // launch (a host-side call) so no state is shared across threads or devices
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_expert_gemm_big_nv<ST, PK, PF>),

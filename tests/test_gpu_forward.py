@@ -90,6 +90,26 @@ def test_cap_forms_under_stress(gpu_lib, form, fmt):
     assert rel_err(r["out"], ref) <= OUT_RTOL
 
 
+# Skewed expert loads (Zipf bias) over 48 experts at about 170 rows each: the
+# experts' last 128-row tiles hold every count of 16-row sub-tiles from 1 to 8
+# (the large-M kernels compile one tile body per count).
+RAGGED = {
+    "nvfp4": synth.Workload("ragged_nvfp4", "ragged last tiles", 2048, 256, 48, 4, 128, "nvfp4", 28,
+                            bias="zipf", weights="gaussian"),
+    "mxfp8": synth.Workload("ragged_mxfp8", "ragged last tiles", 2048, 256, 48, 4, 128, "mxfp8", 29,
+                            bias="zipf", weights="gaussian"),
+}
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+def test_large_m_partial_tiles_every_subtile_count(gpu_lib, fmt):
+    w = RAGGED[fmt]
+    r = run_layer(gpu_lib, w)
+    rem = np.bincount(r["ids"].ravel(), minlength=w.experts) % 128
+    assert set(int(v) for v in np.ceil(rem[rem > 0] / 16)) == set(range(1, 9))
+    assert rel_err(r["out"], oracle_out(w, r)) <= OUT_RTOL
+
+
 def test_single_token_and_max_tokens_margin(gpu_lib):
     w = SMALL["mid_nvfp4"]
     r = run_layer(gpu_lib, w, T=1, max_tokens=300)
@@ -115,11 +135,13 @@ def test_inkling_workloads_sampled(gpu_lib, key, ntok):
     assert np.array_equal(r2["out"], r["out"])
 
 
-@pytest.mark.parametrize("key", ["tiny", "mid_nvfp4", "mid_mxfp8", "ep_nvfp4", "decode_nvfp4", "decode_mxfp8"])
+@pytest.mark.parametrize("key", ["tiny", "mid_nvfp4", "mid_mxfp8", "ep_nvfp4", "ragged_nvfp4", "ragged_mxfp8",
+                                 "decode_nvfp4", "decode_mxfp8"])
 def test_packed_layout_matches_canonical_bit_exact(gpu_lib, key):
     """moe_prepare_weights only permutes bytes: the layer output with packed
     weights is bit-identical to the output with the canonical arrays."""
-    w = SMALL.get(key) or synth.WORKLOADS[key]
+    ragged = {w.key: w for w in RAGGED.values()}
+    w = SMALL.get(key) or ragged.get(key) or synth.WORKLOADS[key]
     a = run_layer(gpu_lib, w, layout="canonical")
     b = run_layer(gpu_lib, w, layout="packed")
     assert np.array_equal(a["ids"], b["ids"])
