@@ -241,14 +241,21 @@ __device__ __forceinline__ void big_mx_tile(const GemmArgs& a, const BigItem& it
   if (STAGE == 0) {
     const float inv_c = 1.0f / a.cap;
     float* amx = reinterpret_cast<float*>(abuf);   // [128 rows][8 waves]
-    float h[NSUB][4];
+    float h[4 * NSUB], u[4 * NSUB];
+#pragma unroll
+    for (int i = 0; i < NSUB; i++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        h[4 * i + q] = acc[i][0][q];
+        u[4 * i + q] = acc[i][1][q];
+      }
+    cap_swiglu_n(h, u, a.cap_form, a.cap, inv_c);
 #pragma unroll
     for (int i = 0; i < NSUB; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 16 * i + 4 * g4 + q;
-        h[i][q] = cap_swiglu(acc[i][0][q], acc[i][1][q], a.cap_form, a.cap, inv_c);
-        float am = m < rows ? fabsf(h[i][q]) : 0.0f;
+        float am = m < rows ? fabsf(h[4 * i + q]) : 0.0f;
 #pragma unroll
         for (int o = 8; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, kWave));
         if (cl == 0) amx[m * 8 + wave] = am;
@@ -263,7 +270,7 @@ __device__ __forceinline__ void big_mx_tile(const GemmArgs& a, const BigItem& it
         if (m >= rows) continue;
         const float am = fmaxf(amx[m * 8 + wave], amx[m * 8 + (wave ^ 1)]);
         const int E = mx_exponent(am);
-        a.out_q[(size_t)(row0 + m) * a.F + col] = (uint8_t)mx_encode(h[i][q], pow2f(-E));
+        a.out_q[(size_t)(row0 + m) * a.F + col] = (uint8_t)mx_encode(h[4 * i + q], pow2f(-E));
         if (cl == 0 && (wave & 1) == 0) a.out_s[(size_t)(row0 + m) * (a.F / 32) + col / 32] = (uint8_t)(E + 127);
       }
   } else {
@@ -444,16 +451,23 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
     const float inv_c = 1.0f / a.cap;
     const float wg = a.w_gs[3 * el + 0], wu = a.w_gs[3 * el + 1];
     const int col = bx * 128 + 16 * wave + cl;
+    float h[4 * NSUB], u[4 * NSUB];
+#pragma unroll
+    for (int i = 0; i < NSUB; i++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const float ga = rgs[16 * i + 4 * g4 + q];
+        h[4 * i + q] = (acc[i][0][q] * ga) * wg;
+        u[4 * i + q] = (acc[i][1][q] * ga) * wu;
+      }
+    cap_swiglu_n(h, u, a.cap_form, a.cap, inv_c);
 #pragma unroll
     for (int i = 0; i < NSUB; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 16 * i + 4 * g4 + q;
         if (m >= rows) continue;
-        const float ga = rgs[m];
-        const float gv = (acc[i][0][q] * ga) * wg;
-        const float uv = (acc[i][1][q] * ga) * wu;
-        a.out[(size_t)(row0 + m) * a.F + col] = cap_swiglu(gv, uv, a.cap_form, a.cap, inv_c);
+        a.out[(size_t)(row0 + m) * a.F + col] = h[4 * i + q];
       }
   } else {
     const float wd = a.w_gs[3 * el + 2];

@@ -111,11 +111,17 @@ __device__ inline float wave_sum(float v) {
 
 __device__ inline float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// Reciprocal from the hardware instruction (v_rcp_f32, within 1 ulp; 1/inf
+// is 0).  The epilogues take their quotients this way: an IEEE division
+// expands to about ten instructions, which in the large-M gate/up epilogue
+// was as much vector-ALU work as the k loop's operand expansion.
+__device__ inline float rcp_fast(float y) { return __builtin_amdgcn_rcpf(y); }
+
 // tanh from one hardware exponential: tanh|x| = 1 - 2 / (e^{2|x|} + 1)
 // (relative error a few 1e-7; e^{2|x|} = inf gives exactly 1).
 __device__ inline float tanh_fast(float x) {
   const float e = __expf(2.0f * fabsf(x));
-  return copysignf(1.0f - __fdividef(2.0f, e + 1.0f), x);
+  return copysignf(1.0f - 2.0f * rcp_fast(e + 1.0f), x);
 }
 
 // Cap + SwiGLU on fp32 gate/up values (cap forms of enum moe_cap_form).
@@ -127,9 +133,36 @@ __device__ inline float cap_swiglu(float g, float u, int form, float c, float in
     g = fminf(g, c);
     u = fminf(fmaxf(u, -c), c);
   }
-  float h = __fdividef(g, 1.0f + __expf(-g)) * u;
+  float h = g * rcp_fast(1.0f + __expf(-g)) * u;
   if (form == 2) h = c * tanh_fast(h * inv_c);
   return h;
+}
+
+// The same on N pairs in place (g[i] <- h[i]), the arithmetic of cap_swiglu
+// per element.  Each form's work sits in its own loop under one uniform
+// branch: with the branch per element the compiler evaluates every form and
+// selects.
+template <int N>
+__device__ inline void cap_swiglu_n(float (&g)[N], float (&u)[N], int form, float c, float inv_c) {
+  if (form == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      g[i] = c * tanh_fast(g[i] * inv_c);
+      u[i] = c * tanh_fast(u[i] * inv_c);
+    }
+  } else if (form == 1) {
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+      g[i] = fminf(g[i], c);
+      u[i] = fminf(fmaxf(u[i], -c), c);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < N; i++) g[i] = g[i] * rcp_fast(1.0f + __expf(-g[i])) * u[i];
+  if (form == 2) {
+#pragma unroll
+    for (int i = 0; i < N; i++) g[i] = c * tanh_fast(g[i] * inv_c);
+  }
 }
 
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
