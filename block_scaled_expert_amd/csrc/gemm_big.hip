@@ -79,14 +79,14 @@ constexpr int kBigHead = 2 * 4 * BM;
 }  // namespace
 
 // A work item of a large-M launch: one row tile of an expert (a dispatch
-// work-list entry) and one weight tile.  Work items are ordered so that the
+// work-list entry) and one of the nx weight tiles.  Work items are ordered so that the
 // items one XCD runs back to back are consecutive row tiles of the same
 // weight tile.  Returns false for workgroups beyond the launch's items.
 struct BigItem {
   int el, row0, rows, bx;
 };
-__device__ inline bool big_item(const GemmArgs& a, int stage, BigItem& it) {
-  const int nt = a.ntiles[0], nx = stage == 0 ? a.F / 128 : a.H / BNW;
+__device__ inline bool big_item(const GemmArgs& a, int nx, BigItem& it) {
+  const int nt = a.ntiles[0];
   const int items = nx * nt;
   const int hw = blockIdx.x;
   if (hw >= items) return false;
@@ -226,7 +226,7 @@ __device__ __forceinline__ void big_mx_tile(const GemmArgs& a, const BigItem& it
     bload(min(step + PF, NS - 1), bring[j]);
     astore((step + 1) & 1, ast[(j + 1) % PF]);
     aload(min(step + 1 + PF, NS - 1), ast[(j + 1) % PF]);
-    __syncthreads();
+    lds_barrier();
   };
   for (int s0 = 0; s0 < NS; s0 += PF) {
     one_step(std::integral_constant<int, 0>{}, s0);
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_mx(GemmArgs a) {
   static_assert(PF >= 1 && PF <= 3, "ring depth");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   BigItem it;
-  if (!big_item(a, STAGE, it)) return;
+  if (!big_item(a, STAGE == 0 ? a.F / 128 : a.H / BNW, it)) return;
   const int tid = threadIdx.x;
   if (tid < BM)
     reinterpret_cast<int*>(lds)[tid] =
@@ -329,7 +329,9 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
   uint8_t* abuf = lds + kBigHead;
   const int el = it.el, row0 = it.row0, rows = it.rows, bx = it.bx;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: readfirstlane puts it (and every address
+  // derived from it alone) in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int K = STAGE == 0 ? a.H : a.F;
   const int NS = K / 128;
@@ -363,6 +365,8 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
 
   // this wave's two column groups of 16 weight rows: gate/up: the gate group
   // and its up group (h columns bx*128 + 16 w ..); down: rows bx*256 + 32 w + 16 c
+  // (uniform row bases in scalar registers, one 32-bit lane offset each for
+  // codes and scales)
   const uint8_t* brow[2];
   const uint8_t* bsrow[2];
 #pragma unroll
@@ -370,18 +374,20 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
     const int n0 = STAGE == 0 ? c * a.F + bx * 128 + 16 * wave : bx * BNW + 32 * wave + 16 * c;
     if (PACKED) {
       const size_t t0 = (size_t)(n0 / 16) * NS;
-      brow[c] = wexp + t0 * 1024 + 16 * lane;
-      bsrow[c] = wsexp + t0 * 128 + 2 * lane;
+      brow[c] = wexp + t0 * 1024;
+      bsrow[c] = wsexp + t0 * 128;
     } else {
-      brow[c] = wexp + (size_t)(n0 + r) * row_bytes + 16 * g;
-      bsrow[c] = wsexp + (size_t)(n0 + r) * sc_bytes + 2 * g;
+      brow[c] = wexp + (size_t)n0 * row_bytes;
+      bsrow[c] = wsexp + (size_t)n0 * sc_bytes;
     }
   }
+  const uint32_t boff = PACKED ? 16 * lane : r * row_bytes + 16 * g;
+  const uint32_t bsoff = PACKED ? 2 * lane : r * sc_bytes + 2 * g;
   auto bload = [&](int s, BFrag4* B) {
 #pragma unroll
     for (int c = 0; c < 2; c++) {
-      B[c].q = *reinterpret_cast<const v4u*>(brow[c] + (PACKED ? (size_t)s * 1024 : (size_t)s * 64));
-      B[c].sc = *reinterpret_cast<const uint16_t*>(bsrow[c] + (PACKED ? s * 128 : s * 8));
+      B[c].q = *reinterpret_cast<const v4u*>(brow[c] + (PACKED ? (size_t)s * 1024 : (size_t)s * 64) + boff);
+      B[c].sc = *reinterpret_cast<const uint16_t*>(bsrow[c] + (PACKED ? s * 128 : s * 8) + bsoff);
     }
   };
 
@@ -389,36 +395,85 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
 #pragma unroll
   for (int i = 0; i < NSUB; i++) acc[i][0] = acc[i][1] = v4f{0, 0, 0, 0};
 
-  auto compute = [&](int buf, const BFrag4* B) {
-    const uint8_t* A = abuf + buf * ABUF;
-    v2h bs[2][2];
+  // One k step on activation buffer `buf`, scheduled by hand as 4 x NSUB
+  // chunks (part j of the step's four 32-wide parts, row sub-tile i), each
+  // fenced by a scheduling barrier.  Chunk (j, i) issues the LDS read of the
+  // next chunk's activation fragment, its own two MFMAs, and an even share
+  // of the vector-ALU work: the expansion of part j+1's weight fragments
+  // (8 convert + multiply pairs per part) and, when STG, of part j of the
+  // next activation tile (4 pairs in the part's last two chunks, then one
+  // LDS store into buffer `nbuf`).
+  // The matrix cores then never wait behind a block of conversions.
+  // `issue_loads` runs at the start of part 3, once this step's weight
+  // fragments are no longer read.
+  auto compute = [&](int buf, const BFrag4* B, int nbuf, const AStage4& st, auto STG, auto&& issue_loads) {
+    constexpr bool stage_here = decltype(STG)::value;
+    constexpr int NC = 4 * NSUB;
+    const uint8_t* A = abuf + buf * ABUF + lane * 16;
+    uint8_t* S = abuf + nbuf * ABUF + wave * 4096 + lane * 16;
+    v2h bs[2][2], as[2];
 #pragma unroll
     for (int c = 0; c < 2; c++) {
       const v2h sp = sig2_of(B[c].sc);
       bs[c][0] = v2h{sp[0], sp[0]};
       bs[c][1] = v2h{sp[1], sp[1]};
     }
+    if constexpr (stage_here) {
+      const v2h sp = sig2_of(st.sc);
+      as[0] = v2h{sp[0], sp[0]};
+      as[1] = v2h{sp[1], sp[1]};
+    }
+    auto word = [](const v4u& q, int j) { return j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w; };
+    // f16 pair p (codes 2p, 2p+1) of word w times the scale pair
+    auto pair = [](uint32_t w, int p, v2h sc) {
+      const v2h f = p == 0 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0)
+                  : p == 1 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1)
+                  : p == 2 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2)
+                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3);
+      return f * sc;
+    };
+    auto pack = [](const v2h (&x)[4]) {
+      return v8h{x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
+    };
+    v2h bx[2][2][4];   // [part parity][column group][pair]
+    v2h sx[4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int c = 0; c < 2; c++)
+#pragma unroll
+      for (int p = 0; p < 4; p++) bx[0][c][p] = pair(word(B[c].q, 0), p, bs[c][0]);
+    v8h av[2];
+    av[0] = *reinterpret_cast<const v8h*>(A);
+#pragma unroll
+    for (int t = 0; t < NC; t++) {
+      const int j = t / NSUB, i = t % NSUB;
       __builtin_amdgcn_sched_barrier(0);
-      v8h bv[2];
-#pragma unroll
-      for (int c = 0; c < 2; c++) {
-        const uint32_t w = j == 0 ? B[c].q.x : j == 1 ? B[c].q.y : j == 2 ? B[c].q.z : B[c].q.w;
-        bv[c] = dq8(w, j < 2 ? bs[c][0] : bs[c][1]);
+      if (t == 3 * NSUB) issue_loads();
+      if (t + 1 < NC) {
+        const int jn = (t + 1) / NSUB, in = (t + 1) % NSUB;
+        av[(t + 1) & 1] = *reinterpret_cast<const v8h*>(A + in * 4096 + jn * 1024);
       }
+      const v8h b0 = pack(bx[j & 1][0]), b1 = pack(bx[j & 1][1]);
+      acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t & 1], b0, acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t & 1], b1, acc[i][1], 0, 0, 0);
+      if (j < 3) {
 #pragma unroll
-      for (int i = 0; i < NSUB; i++) {
-        const v8h av = *reinterpret_cast<const v8h*>(A + i * 4096 + j * 1024 + lane * 16);
+        for (int k = 0; k < 8; k++)
+          if (k * NSUB / 8 == i) bx[(j + 1) & 1][k >> 2][k & 3] = pair(word(B[k >> 2].q, j + 1), k & 3, bs[k >> 2][(j + 1) >> 1]);
+      }
+      if constexpr (stage_here) {
 #pragma unroll
-        for (int c = 0; c < 2; c++)
-          acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[c], acc[i][c], 0, 0, 0);
+        for (int k = 0; k < 4; k++)
+          if (NSUB - 2 + k / 2 == i) sx[k] = pair(word(st.q, j), k, as[j >> 1]);
+        if (i == NSUB - 1) *reinterpret_cast<v8h*>(S + j * 1024) = pack(sx);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // main loop: PF steps of weights and activations in flight (as in
-  // big_mx_tile; ring slots are compile-time constants)
+  // big_mx_tile; ring slots are compile-time constants).  Full tiles stage
+  // the next activation tile inside compute; partial tiles (only the first
+  // NSUB waves stage) after it.
   BFrag4 bring[PF][2];
   AStage4 ast[PF];
 #pragma unroll
@@ -432,11 +487,19 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
   auto one_step = [&](auto J, int s0) {
     constexpr int j = decltype(J)::value;
     const int step = s0 + j;
-    compute(step & 1, bring[j]);
-    bload(min(step + PF, NS - 1), bring[j]);
-    astore((step + 1) & 1, ast[(j + 1) % PF]);
-    aload(min(step + 1 + PF, NS - 1), ast[(j + 1) % PF]);
-    __syncthreads();
+    AStage4& nst = ast[(j + 1) % PF];
+    // with one step in flight the next weights reuse this step's ring slot,
+    // loaded once part 3 runs; deeper rings load after the step
+    auto next_b = [&] { if constexpr (PF == 1) bload(min(step + PF, NS - 1), bring[j]); };
+    if constexpr (NSUB == 8) {
+      compute(step & 1, bring[j], (step + 1) & 1, nst, std::true_type{}, next_b);
+    } else {
+      compute(step & 1, bring[j], (step + 1) & 1, nst, std::false_type{}, next_b);
+      astore((step + 1) & 1, nst);
+    }
+    if constexpr (PF > 1) bload(min(step + PF, NS - 1), bring[j]);
+    aload(min(step + 1 + PF, NS - 1), nst);
+    lds_barrier();
   };
   for (int s0 = 0; s0 < NS; s0 += PF) {
     one_step(std::integral_constant<int, 0>{}, s0);
@@ -490,7 +553,7 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
   static_assert(PF >= 1 && PF <= 3, "ring depth");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   BigItem it;
-  if (!big_item(a, STAGE, it)) return;
+  if (!big_item(a, STAGE == 0 ? a.F / 128 : a.H / BNW, it)) return;
   const int tid = threadIdx.x;
   if (tid < BM) {
     const int tk = tid < it.rows ? (STAGE == 0 ? a.sorted[it.row0 + tid] / a.k : it.row0 + tid) : -1;
@@ -509,6 +572,7 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
     default: big_nv_tile<STAGE, PACKED, PF, 8>(a, it, lds); break;
   }
 }
+
 
 namespace {
 

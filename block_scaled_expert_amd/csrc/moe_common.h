@@ -89,6 +89,19 @@ __host__ __device__ inline int mx_exponent(float amax) {
 // the scaling is exact, the encode rounds once.
 __device__ inline uint32_t mx_encode(float v, float step) { return e4m3_encode(__fmul_rn(v, step)); }
 
+// Workgroup barrier for hand-offs through LDS: waits for the wave's own LDS
+// operations, then for every wave.  HIP's __syncthreads also waits for all
+// of the wave's outstanding global loads, which in a k loop that prefetches
+// the next step through registers stalls every step for a full memory round
+// trip; here those loads stay in flight (the compiler waits for each at its
+// first use).
+__device__ inline void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ inline float bf16_to_f32(uint16_t h) { return bits_f((uint32_t)h << 16); }
 
 // fp32 -> bf16, round to nearest even (finite inputs).

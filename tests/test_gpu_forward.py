@@ -96,12 +96,14 @@ def test_cap_forms_under_stress(gpu_lib, form, fmt):
 RAGGED = {
     "nvfp4": synth.Workload("ragged_nvfp4", "ragged last tiles", 2048, 256, 48, 4, 128, "nvfp4", 28,
                             bias="zipf", weights="gaussian"),
+    "nvfp4_wide": synth.Workload("ragged_nvfp4_wide", "ragged last tiles", 2048, 512, 48, 4, 256, "nvfp4", 30,
+                                 bias="zipf", weights="gaussian"),
     "mxfp8": synth.Workload("ragged_mxfp8", "ragged last tiles", 2048, 256, 48, 4, 128, "mxfp8", 29,
                             bias="zipf", weights="gaussian"),
 }
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+@pytest.mark.parametrize("fmt", list(RAGGED))
 def test_large_m_partial_tiles_every_subtile_count(gpu_lib, fmt):
     w = RAGGED[fmt]
     r = run_layer(gpu_lib, w)
@@ -135,8 +137,8 @@ def test_inkling_workloads_sampled(gpu_lib, key, ntok):
     assert np.array_equal(r2["out"], r["out"])
 
 
-@pytest.mark.parametrize("key", ["tiny", "mid_nvfp4", "mid_mxfp8", "ep_nvfp4", "ragged_nvfp4", "ragged_mxfp8",
-                                 "decode_nvfp4", "decode_mxfp8"])
+@pytest.mark.parametrize("key", ["tiny", "mid_nvfp4", "mid_mxfp8", "ep_nvfp4", "ragged_nvfp4", "ragged_nvfp4_wide",
+                                 "ragged_mxfp8", "decode_nvfp4", "decode_mxfp8"])
 def test_packed_layout_matches_canonical_bit_exact(gpu_lib, key):
     """moe_prepare_weights only permutes bytes: the layer output with packed
     weights is bit-identical to the output with the canonical arrays."""
