@@ -43,8 +43,12 @@ __device__ inline v8h dq8(uint32_t word, v2h sig2) {
   return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 // two E4M3 bytes -> f16 pair {sigma0, sigma1} * 2^-8 (field move, see gemm.hip)
+// (the two bytes are first spread to the halves, {b0, 0, b1, 0}, so every
+// shift is by an inline constant and no shift amount or selector has to be
+// held in a vector register)
 __device__ inline v2h sig2_of(uint32_t w) {
-  const uint32_t b = ((w & 0x7Fu) << 7) | ((w & 0x80u) << 8) | ((w & 0x7F00u) << 15) | ((w & 0x8000u) << 16);
+  const uint32_t x = (w & 0xFFu) | ((w & 0xFF00u) << 8);
+  const uint32_t b = ((x & 0x007F007Fu) << 7) | ((x & 0x00800080u) << 8);
   return __builtin_bit_cast(v2h, b);
 }
 
@@ -441,20 +445,23 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
     for (int c = 0; c < 2; c++)
 #pragma unroll
       for (int p = 0; p < 4; p++) bx[0][c][p] = pair(word(B[c].q, 0), p, bs[c][0]);
-    v8h av[2];
-    av[0] = *reinterpret_cast<const v8h*>(A);
+    constexpr int AR = 3;   // activation fragments in flight: reads run two chunks ahead
+    v8h av[AR];
+#pragma unroll
+    for (int t = 0; t < AR - 1 && t < NC; t++)
+      av[t] = *reinterpret_cast<const v8h*>(A + (t % NSUB) * 4096 + (t / NSUB) * 1024);
 #pragma unroll
     for (int t = 0; t < NC; t++) {
       const int j = t / NSUB, i = t % NSUB;
       __builtin_amdgcn_sched_barrier(0);
       if (t == 3 * NSUB) issue_loads();
-      if (t + 1 < NC) {
-        const int jn = (t + 1) / NSUB, in = (t + 1) % NSUB;
-        av[(t + 1) & 1] = *reinterpret_cast<const v8h*>(A + in * 4096 + jn * 1024);
+      if (t + AR - 1 < NC) {
+        const int tn = t + AR - 1, jn = tn / NSUB, in = tn % NSUB;
+        av[tn % AR] = *reinterpret_cast<const v8h*>(A + in * 4096 + jn * 1024);
       }
       const v8h b0 = pack(bx[j & 1][0]), b1 = pack(bx[j & 1][1]);
-      acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t & 1], b0, acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t & 1], b1, acc[i][1], 0, 0, 0);
+      acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t % AR], b0, acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[t % AR], b1, acc[i][1], 0, 0, 0);
       if (j < 3) {
 #pragma unroll
         for (int k = 0; k < 8; k++)
