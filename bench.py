@@ -81,18 +81,29 @@ def gemm_source(workload: str) -> str:
     return "gemm.hip" if small else "gemm_big.hip"
 
 
+GEMM_HEADERS = ("moe_common.h", "launch.h")   # included by both GEMM sources
+
+
+def gemm_source_sha256(fname: str) -> str:
+    """sha256 over the GEMM source file and the headers it includes, in that
+    order: a change to any of them changes the compiled kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (fname, *GEMM_HEADERS):
+        h.update(open(os.path.join(ROOT, "block_scaled_expert_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes (fetch + write) per launch of `kernel` ("gate_up" / "down")
     recorded from rocprofv3 counters in profiles/traffic.json, if the GEMM
-    source has not changed since; else None."""
-    import hashlib
+    source and its headers have not changed since; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(workload)
     fname = gemm_source(workload)
-    src = open(os.path.join(ROOT, "block_scaled_expert_amd", "csrc", fname), "rb").read()
-    if (not rec or rec.get("source_file") != fname or rec.get("source_sha256") != hashlib.sha256(src).hexdigest()
+    if (not rec or rec.get("source_file") != fname or rec.get("source_sha256") != gemm_source_sha256(fname)
             or kernel not in rec):
         return None
     return rec[kernel]["fetch_bytes"] + rec[kernel]["write_bytes"]
