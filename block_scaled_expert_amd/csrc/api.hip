@@ -358,13 +358,19 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   d.w_codes = w->w2;
   d.w_sc = w->w2_sc;
   d.out = at<float>(ws, L.y);
+  // y larger than the last-level cache streams (non-temporal stores in the
+  // down epilogue, loads in the combine); its size is taken at the expected
+  // local pair count, the one the tile height follows
+  const size_t y_bytes = (size_t)T * k * EL / c->num_experts * H * sizeof(float);
+  const bool stream_y = y_bytes > kStreamBytes;
+  d.stream_out = stream_y ? 1 : 0;
   record(events, 2 * MOE_STAGE_DOWN, s);
   bad |= launch_gemm_down(d, s);
   record(events, 2 * MOE_STAGE_DOWN + 1, s);
 
   // 6. combine
   record(events, 2 * MOE_STAGE_COMBINE, s);
-  bad |= launch_combine(at<float>(ws, L.y), b.pos, topk_w, T, k, H, static_cast<uint16_t*>(out), s);
+  bad |= launch_combine(at<float>(ws, L.y), b.pos, topk_w, T, k, H, stream_y, static_cast<uint16_t*>(out), s);
   record(events, 2 * MOE_STAGE_COMBINE + 1, s);
   (void)nv;
   return bad ? MOE_ERR_LAUNCH : MOE_OK;

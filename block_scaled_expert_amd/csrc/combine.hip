@@ -3,12 +3,15 @@
 // "combine" stage of the SGLang cookbook's MegaMoE description, section 2).
 // y rows are in expert-sorted order; pair_pos maps pair t*k + j to its row
 // (-1: expert not local).  One workgroup per (token, 1024 columns), fp32
-// accumulation, no atomics.  HBM-bound: reads k rows of fp32 y, writes one bf16 row.
+// accumulation, no atomics.  HBM-bound: reads k rows of fp32 y, writes one
+// bf16 row.  y larger than the last-level cache is read with the
+// non-temporal hint (NT).
 #include "moe_common.h"
 #include "launch.h"
 
 namespace moe {
 
+template <bool NT>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const int32_t* __restrict__ pos,
                                                  const float* __restrict__ w, int k, int H,
                                                  uint16_t* __restrict__ out) {
@@ -22,7 +25,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
       const int p = pt[j];
       if (p < 0) continue;
       const float wj = wt[j];
-      const float4 v = reinterpret_cast<const float4*>(y + (size_t)p * H)[c];
+      const v4f* yp = reinterpret_cast<const v4f*>(y + (size_t)p * H) + c;
+      const v4f v = NT ? __builtin_nontemporal_load(yp) : *yp;
       acc.x += wj * v.x;
       acc.y += wj * v.y;
       acc.z += wj * v.z;
@@ -34,10 +38,12 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
   }
 }
 
-int launch_combine(const float* y, const int32_t* pos, const float* w, int T, int k, int H,
+int launch_combine(const float* y, const int32_t* pos, const float* w, int T, int k, int H, bool nt,
                    uint16_t* out, hipStream_t stream) {
   if (T <= 0) return 0;
-  hipLaunchKernelGGL(k_combine, dim3(T, ceil_div(H / 4, 256)), dim3(256), 0, stream, y, pos, w, k, H, out);
+  const dim3 grid(T, ceil_div(H / 4, 256));
+  if (nt) hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, stream, y, pos, w, k, H, out);
+  else hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, stream, y, pos, w, k, H, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -20,7 +20,9 @@
 //  - MXFP8 (k_expert_gemm_big_mx): the gate/up epilogue encodes h to MXFP8
 //    directly.  NVFP4 (k_expert_gemm_big_nv): see there.
 // Each weight element is fetched once per 128 rows of an expert; the
-// activation tile once per 256 weight rows.  Work items (row tile, weight
+// activation tile once per 256 weight rows.  Down rows larger in total than
+// the last-level cache are written with non-temporal stores (GemmArgs
+// stream_out).  Work items (row tile, weight
 // tile) are ordered so that the items one XCD runs back to back are
 // consecutive row tiles of the same weight tile: the hardware hands
 // workgroups to the 8 XCDs round-robin, and each XCD has its own L2.
@@ -79,6 +81,12 @@ constexpr int abuf_bytes() {
 // LDS bytes ahead of the activation buffers: the tile rows' token indices
 // and (NVFP4) their activation scales.
 constexpr int kBigHead = 2 * 4 * BM;
+
+// one fp32 down output; the flag is uniform over the launch
+__device__ inline void put_out(const GemmArgs& a, size_t idx, float v) {
+  if (a.stream_out) __builtin_nontemporal_store(v, a.out + idx);
+  else a.out[idx] = v;
+}
 
 }  // namespace
 
@@ -285,7 +293,7 @@ __device__ __forceinline__ void big_mx_tile(const GemmArgs& a, const BigItem& it
         const int m = 16 * i + 4 * g4 + q;
         if (m >= rows) continue;
 #pragma unroll
-        for (int c = 0; c < 2; c++) a.out[(size_t)(row0 + m) * a.H + bx * BNW + 32 * wave + 16 * c + cl] = acc[i][c][q];
+        for (int c = 0; c < 2; c++) put_out(a, (size_t)(row0 + m) * a.H + bx * BNW + 32 * wave + 16 * c + cl, acc[i][c][q]);
       }
   }
 }
@@ -550,7 +558,7 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
         const float ha = rgs[m];
 #pragma unroll
         for (int c = 0; c < 2; c++)
-          a.out[(size_t)(row0 + m) * a.H + bx * BNW + 32 * wave + 16 * c + cl] = (acc[i][c][q] * ha) * wd;
+          put_out(a, (size_t)(row0 + m) * a.H + bx * BNW + 32 * wave + 16 * c + cl, (acc[i][c][q] * ha) * wd);
       }
   }
 }

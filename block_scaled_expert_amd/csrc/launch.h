@@ -84,7 +84,14 @@ struct GemmArgs {
   // scales [P][F/32] instead of being written to `out`
   uint8_t* out_q;
   uint8_t* out_s;
+  // down only: `out` is larger than the last-level cache, written with
+  // non-temporal stores (the combine then streams it back)
+  int stream_out;
 };
+// Buffers above this size (MI355X's 256 MiB last-level cache) are written
+// and read back with the non-temporal hint; below it, the consumer finds
+// them in the cache.
+constexpr size_t kStreamBytes = size_t(256) << 20;
 int gemm_tile_m(int T, int k, int E);
 // LDS-staged variant for 128-row work-list entries (gemm_big.hip); needs
 // H % 256 == 0 and F % 128 == 0.
@@ -98,7 +105,7 @@ int launch_gemm_down(const GemmArgs& a, hipStream_t stream);
 int launch_pack(int fmt, const uint8_t* codes, const uint8_t* scales, long nmat, int N, int K,
                 uint8_t* pcodes, uint8_t* pscales, hipStream_t stream);
 
-int launch_combine(const float* y, const int32_t* pos, const float* w, int T, int k, int H,
+int launch_combine(const float* y, const int32_t* pos, const float* w, int T, int k, int H, bool nt,
                    uint16_t* out, hipStream_t stream);
 
 }  // namespace moe
