@@ -86,16 +86,19 @@ __global__ __launch_bounds__(256) void k_router_logits_split(const uint16_t* __r
   }
 }
 
-// Larger batches: a workgroup of 4 waves (2 x 2) computes a 128-token x
+// Larger batches: a workgroup of 8 waves (2 x 4) computes a 128-token x
 // 128-expert tile over one K slice (grid z = split).  Each 64-wide k step of
 // both operands is staged in LDS in MFMA lane order (chunk q of 16 bytes at
 // byte 16 q: row tile q/128, k half (q/64)%2, lane q%64), so every wavefront
-// store and load is 1 KB contiguous; the next step is fetched into registers
-// while the current one is multiplied.  Each wave owns 64 x 64 outputs over
-// the whole slice and writes its partial plane directly.
-__global__ __launch_bounds__(256) void k_router_logits_tiled(const uint16_t* __restrict__ x, int T, int H,
-                                                             const uint16_t* __restrict__ wr, int E, int S,
-                                                             float* __restrict__ zpart) {
+// store and load is 1 KB contiguous; the steps after the current one are
+// fetched into registers while it is multiplied.  Each wave owns 64 tokens x
+// 32 experts over the whole slice (half the accumulators of a 2 x 2
+// arrangement), so the kernel fits 128 registers and two workgroups share a
+// CU (4 waves per SIMD); each wave writes its partial plane directly.  Every
+// output's k order is the same as in one wave: step by step, both halves.
+__global__ __launch_bounds__(512, 4) void k_router_logits_tiled(const uint16_t* __restrict__ x, int T, int H,
+                                                                const uint16_t* __restrict__ wr, int E, int S,
+                                                                float* __restrict__ zpart) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][16384];   // [buffer][A, B][8 tiles x 2 halves x 64 lanes x 16 B]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave & 1, wn = wave >> 1;
@@ -103,53 +106,52 @@ __global__ __launch_bounds__(256) void k_router_logits_tiled(const uint16_t* __r
   const int nsteps = H / 64;
   const int s_lo = split * nsteps / S, s_hi = (split + 1) * nsteps / S;
 
-  // staging: thread takes chunks q = tid + 256 u (u < 4) of each operand;
+  // staging: thread takes chunks q = tid + 512 u (u < 2) of each operand;
   // rows past T / E read a valid row (their sums are never stored)
-  const uint16_t* ap[4];
-  const uint16_t* bp[4];
+  const uint16_t* ap[2];
+  const uint16_t* bp[2];
 #pragma unroll
-  for (int u = 0; u < 4; u++) {
-    const int q = tid + 256 * u, f = q >> 7, hh = (q >> 6) & 1, l = q & 63;
+  for (int u = 0; u < 2; u++) {
+    const int q = tid + 512 * u, f = q >> 7, hh = (q >> 6) & 1, l = q & 63;
     const int koff = 32 * hh + 8 * (l >> 4);
     ap[u] = x + (size_t)min(t0 + 16 * f + (l & 15), T - 1) * H + koff;
     bp[u] = wr + (size_t)min(e0 + 16 * f + (l & 15), E - 1) * H + koff;
   }
   // two register stages: a step's global loads are issued two steps before
   // its MFMAs (one step before its LDS store)
-  v4u ra[2][4], rb[2][4];
-  auto gload = [&](int st, v4u (&sa)[4], v4u (&sb)[4]) {
+  v4u ra[2][2], rb[2][2];
+  auto gload = [&](int st, v4u (&sa)[2], v4u (&sb)[2]) {
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
+    for (int u = 0; u < 2; u++) {
       sa[u] = *reinterpret_cast<const v4u*>(ap[u] + st * 64);
       sb[u] = *reinterpret_cast<const v4u*>(bp[u] + st * 64);
     }
   };
-  auto lstore = [&](int buf, const v4u (&sa)[4], const v4u (&sb)[4]) {
+  auto lstore = [&](int buf, const v4u (&sa)[2], const v4u (&sb)[2]) {
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      *reinterpret_cast<v4u*>(&lds[buf][0][16 * (tid + 256 * u)]) = sa[u];
-      *reinterpret_cast<v4u*>(&lds[buf][1][16 * (tid + 256 * u)]) = sb[u];
+    for (int u = 0; u < 2; u++) {
+      *reinterpret_cast<v4u*>(&lds[buf][0][16 * (tid + 512 * u)]) = sa[u];
+      *reinterpret_cast<v4u*>(&lds[buf][1][16 * (tid + 512 * u)]) = sb[u];
     }
   };
 
-  v4f acc[4][4];
+  v4f acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = v4f{0, 0, 0, 0};
+  for (int i = 0; i < 4; i++) acc[i][0] = acc[i][1] = v4f{0, 0, 0, 0};
   auto mma = [&](int buf) {
 #pragma unroll
     for (int hh = 0; hh < 2; hh++) {
-      v4u av[4], bv[4];
+      v4u av[4], bv[2];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
+      for (int i = 0; i < 4; i++)
         av[i] = *reinterpret_cast<const v4u*>(&lds[buf][0][16 * ((4 * wm + i) * 128 + hh * 64 + lane)]);
-        bv[i] = *reinterpret_cast<const v4u*>(&lds[buf][1][16 * ((4 * wn + i) * 128 + hh * 64 + lane)]);
-      }
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        bv[j] = *reinterpret_cast<const v4u*>(&lds[buf][1][16 * ((2 * wn + j) * 128 + hh * 64 + lane)]);
 #pragma unroll
       for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av[i]),
                                                               __builtin_bit_cast(v8bf, bv[j]), acc[i][j], 0, 0, 0);
     }
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(256) void k_router_logits_tiled(const uint16_t* __r
     }
   }
   // acc reg q of lane l in tile (i, j): token row 16 i + 4 (l/16) + q of the
-  // wave's 64, expert column 16 j + l%16
+  // wave's 64, expert column 16 j + l%16 of its 32
   const int r = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; i++)
@@ -185,8 +187,8 @@ __global__ __launch_bounds__(256) void k_router_logits_tiled(const uint16_t* __r
       const int t = t0 + 64 * wm + 16 * i + 4 * g + q;
       if (t >= T) continue;
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int e = e0 + 64 * wn + 16 * j + r;
+      for (int j = 0; j < 2; j++) {
+        const int e = e0 + 32 * wn + 16 * j + r;
         if (e < E) zpart[((size_t)split * T + t) * E + e] = acc[i][j][q];
       }
     }
@@ -330,7 +332,7 @@ int launch_router(const uint16_t* x, int T, int H, const uint16_t* wr, const flo
     else hipLaunchKernelGGL((k_router_logits_split<4>), grid, dim3(256), 0, stream, x, T, H, wr, E, S, z);
   } else {
     const dim3 grid(ceil_div(T, 128), ceil_div(E, 128), S);
-    hipLaunchKernelGGL(k_router_logits_tiled, grid, dim3(256), 0, stream, x, T, H, wr, E, S, z);
+    hipLaunchKernelGGL(k_router_logits_tiled, grid, dim3(512), 0, stream, x, T, H, wr, E, S, z);
   }
   const dim3 tg(ceil_div(T, 4));
 #define MOE_TOPK(N) \
