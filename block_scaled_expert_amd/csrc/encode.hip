@@ -69,15 +69,20 @@ __global__ __launch_bounds__(256) void k_encode_nvfp4(const InT* __restrict__ w,
   float ab = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; i++) ab = fmaxf(ab, fabsf(v[i]));
-  uint32_t sc = e4m3_encode(__fdiv_rn(ab, __fmul_rn(6.0f, gs)));
+  uint32_t sc = e4m3_hw(__fdiv_rn(ab, __fmul_rn(6.0f, gs)));
   const float sigma = e4m3_decode(sc);
   uint32_t w0 = 0, w1 = 0;
   if (A != 0.0f && sigma != 0.0f) {
     const float r = __fdiv_rn(1.0f, __fmul_rn(sigma, gs));
+    if (r <= 3.4028235e38f) {   // r overflows only where the row (or matrix) maximum is below ~4e-33
+      w0 = e2m1_pack8(v, r);
+      w1 = e2m1_pack8(v + 8, r);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; i++) w0 |= e2m1_encode(__fmul_rn(v[i], r)) << (4 * i);
+      for (int i = 0; i < 8; i++) w0 |= e2m1_encode(__fmul_rn(v[i], r)) << (4 * i);
 #pragma unroll
-    for (int i = 0; i < 8; i++) w1 |= e2m1_encode(__fmul_rn(v[8 + i], r)) << (4 * i);
+      for (int i = 0; i < 8; i++) w1 |= e2m1_encode(__fmul_rn(v[8 + i], r)) << (4 * i);
+    }
   }
   if (A == 0.0f) sc = 0;
   *reinterpret_cast<uint2*>(codes + e0 / 2) = make_uint2(w0, w1);

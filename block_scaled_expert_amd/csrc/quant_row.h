@@ -81,15 +81,20 @@ __device__ inline void quant_row_nvfp4(const InT* __restrict__ xr, int cols, int
     float ab = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; i++) ab = fmaxf(ab, fabsf(v[i]));
-    uint32_t sc = e4m3_encode(__fdiv_rn(ab, denom));
+    uint32_t sc = e4m3_hw(__fdiv_rn(ab, denom));
     const float sigma = e4m3_decode(sc);
     uint32_t w0 = 0, w1 = 0;
     if (!zero_row && sigma != 0.0f) {
       const float r = __fdiv_rn(1.0f, __fmul_rn(sigma, gs));
+      if (r <= 3.4028235e38f) {   // r overflows only where the row (or matrix) maximum is below ~4e-33
+        w0 = e2m1_pack8(v, r);
+        w1 = e2m1_pack8(v + 8, r);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; i++) w0 |= e2m1_encode(__fmul_rn(v[i], r)) << (4 * i);
+        for (int i = 0; i < 8; i++) w0 |= e2m1_encode(__fmul_rn(v[i], r)) << (4 * i);
 #pragma unroll
-      for (int i = 0; i < 8; i++) w1 |= e2m1_encode(__fmul_rn(v[8 + i], r)) << (4 * i);
+        for (int i = 0; i < 8; i++) w1 |= e2m1_encode(__fmul_rn(v[8 + i], r)) << (4 * i);
+      }
     }
     if (zero_row) sc = 0;
     if (live) {
@@ -115,11 +120,9 @@ __device__ inline void quant_row_mxfp8(const InT* __restrict__ xr, int cols, int
     const float step = pow2f(-E);   // -E in [-119, 127]
     uint32_t w[8];
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      w[j] = 0;
-#pragma unroll
-      for (int i = 0; i < 4; i++) w[j] |= e4m3_encode(__fmul_rn(v[4 * j + i], step)) << (8 * i);
-    }
+    for (int j = 0; j < 8; j++)
+      w[j] = e4m3_pack4(__fmul_rn(v[4 * j], step), __fmul_rn(v[4 * j + 1], step), __fmul_rn(v[4 * j + 2], step),
+                        __fmul_rn(v[4 * j + 3], step));
     if (live) {
       v4u* dst = reinterpret_cast<v4u*>(cr + 32 * b);
       dst[0] = v4u{w[0], w[1], w[2], w[3]};
