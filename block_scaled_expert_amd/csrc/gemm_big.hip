@@ -336,8 +336,8 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_mx(GemmArgs a) {
 template <int STAGE, bool PACKED, int PF, int NSUB>
 __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it, uint8_t* lds) {
   constexpr int ABUF = abuf_bytes<1>();
-  const int* tok = reinterpret_cast<const int*>(lds);
-  const float* rgs = reinterpret_cast<const float*>(lds + 4 * BM);
+  int* tok = reinterpret_cast<int*>(lds);
+  float* rgs = reinterpret_cast<float*>(lds + 4 * BM);
   uint8_t* abuf = lds + kBigHead;
   const int el = it.el, row0 = it.row0, rows = it.rows, bx = it.bx;
 
@@ -351,29 +351,6 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
   const int row_bytes = K / 2, sc_bytes = K / 16;
   const uint8_t* wexp = a.w_codes + (size_t)el * NW * row_bytes;
   const uint8_t* wsexp = a.w_sc + (size_t)el * NW * sc_bytes;
-
-  // activation staging as in big_mx_tile (wave w < NSUB: row tile w; NVFP4
-  // expanded to f16 on the way into LDS)
-  const bool stager = NSUB == 8 || wave < NSUB;
-  const int ar = 16 * wave + r, aq = g;
-  const int at = tok[ar] >= 0 ? tok[ar] : tok[0];
-  const uint8_t* acode = a.a_codes + (size_t)at * row_bytes + 16 * aq;
-  const uint8_t* asc = a.a_sc + (size_t)at * sc_bytes + 2 * aq;
-  auto aload = [&](int s, AStage4& st) {
-    if (!stager) return;
-    st.q = *reinterpret_cast<const v4u*>(acode + s * 64);
-    st.sc = *reinterpret_cast<const uint16_t*>(asc + s * 8);
-  };
-  auto astore = [&](int buf, const AStage4& st) {
-    if (!stager) return;
-    const v2h sp = sig2_of(st.sc);
-    const v2h s0 = v2h{sp[0], sp[0]}, s1 = v2h{sp[1], sp[1]};
-    uint8_t* base = abuf + buf * ABUF + wave * 4096 + lane * 16;
-    *reinterpret_cast<v8h*>(base + 0 * 1024) = dq8(st.q.x, s0);
-    *reinterpret_cast<v8h*>(base + 1 * 1024) = dq8(st.q.y, s0);
-    *reinterpret_cast<v8h*>(base + 2 * 1024) = dq8(st.q.z, s1);
-    *reinterpret_cast<v8h*>(base + 3 * 1024) = dq8(st.q.w, s1);
-  };
 
   // this wave's two column groups of 16 weight rows: gate/up: the gate group
   // and its up group (h columns bx*128 + 16 w ..); down: rows bx*256 + 32 w + 16 c
@@ -489,16 +466,53 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
   // big_mx_tile; ring slots are compile-time constants).  Full tiles stage
   // the next activation tile inside compute; partial tiles (only the first
   // NSUB waves stage) after it.
+  // Prologue: the tile rows' token indices (threads < 128), then the first
+  // weight steps, which do not depend on them (memory operations complete in
+  // issue order, so the index loads are not held up), then the indices are
+  // published through LDS.  The row scales are needed only by the epilogue:
+  // their loads stay in flight through the main loop.
+  // (No load sits under a branch -- the compiler would drain every
+  // outstanding load where the branch joins -- so every thread loads an
+  // index of the tile, clamped to its last row, and selects afterwards.)
+  const int m_own = min(tid % BM, rows - 1);
+  const int tk_any = STAGE == 0 ? a.sorted[row0 + m_own] / a.k : row0 + m_own;
   BFrag4 bring[PF][2];
+#pragma unroll
+  for (int j = 0; j < PF; j++) bload(min(j, NS - 1), bring[j]);
+  const bool own_row = tid < BM && tid < rows;
+  if (tid < BM) tok[tid] = own_row ? tk_any : -1;
+  const float gs_any = a.a_gs[tk_any];
+  lds_barrier();
+
+  // activation staging as in big_mx_tile (wave w < NSUB: row tile w; NVFP4
+  // expanded to f16 on the way into LDS)
+  const bool stager = NSUB == 8 || wave < NSUB;
+  const int ar = 16 * wave + r, aq = g;
+  const int at = tok[ar] >= 0 ? tok[ar] : tok[0];
+  const uint8_t* acode = a.a_codes + (size_t)at * row_bytes + 16 * aq;
+  const uint8_t* asc = a.a_sc + (size_t)at * sc_bytes + 2 * aq;
+  auto aload = [&](int s, AStage4& st) {
+    if (!stager) return;
+    st.q = *reinterpret_cast<const v4u*>(acode + s * 64);
+    st.sc = *reinterpret_cast<const uint16_t*>(asc + s * 8);
+  };
+  auto astore = [&](int buf, const AStage4& st) {
+    if (!stager) return;
+    const v2h sp = sig2_of(st.sc);
+    const v2h s0 = v2h{sp[0], sp[0]}, s1 = v2h{sp[1], sp[1]};
+    uint8_t* base = abuf + buf * ABUF + wave * 4096 + lane * 16;
+    *reinterpret_cast<v8h*>(base + 0 * 1024) = dq8(st.q.x, s0);
+    *reinterpret_cast<v8h*>(base + 1 * 1024) = dq8(st.q.y, s0);
+    *reinterpret_cast<v8h*>(base + 2 * 1024) = dq8(st.q.z, s1);
+    *reinterpret_cast<v8h*>(base + 3 * 1024) = dq8(st.q.w, s1);
+  };
+
   AStage4 ast[PF];
 #pragma unroll
-  for (int j = 0; j < PF; j++) {
-    bload(min(j, NS - 1), bring[j]);
-    aload(min(j, NS - 1), ast[j]);
-  }
+  for (int j = 0; j < PF; j++) aload(min(j, NS - 1), ast[j]);
   astore(0, ast[0]);
   aload(min(PF, NS - 1), ast[0]);
-  __syncthreads();
+  lds_barrier();
   auto one_step = [&](auto J, int s0) {
     constexpr int j = decltype(J)::value;
     const int step = s0 + j;
@@ -521,6 +535,11 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
     if constexpr (PF > 1) one_step(std::integral_constant<int, 1>{}, s0);
     if constexpr (PF > 2) one_step(std::integral_constant<int, 2>{}, s0);
   }
+
+  // row scales into LDS for the epilogue (the main loop's last barrier has
+  // passed: nothing reads that LDS any more)
+  if (tid < BM) rgs[tid] = own_row ? gs_any : 0.0f;
+  lds_barrier();
 
   // epilogue: acc reg q of lane l in tile (i, c): row 16 i + 4 (l/16) + q,
   // weight row 16 * (group c) + l%16
@@ -569,13 +588,6 @@ __global__ __launch_bounds__(512, 4) void k_expert_gemm_big_nv(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   BigItem it;
   if (!big_item(a, STAGE == 0 ? a.F / 128 : a.H / BNW, it)) return;
-  const int tid = threadIdx.x;
-  if (tid < BM) {
-    const int tk = tid < it.rows ? (STAGE == 0 ? a.sorted[it.row0 + tid] / a.k : it.row0 + tid) : -1;
-    reinterpret_cast<int*>(lds)[tid] = tk;
-    reinterpret_cast<float*>(lds + 4 * BM)[tid] = tk >= 0 ? a.a_gs[tk] : 0.0f;
-  }
-  __syncthreads();
   switch (big_subtiles(it.rows)) {
     case 1: big_nv_tile<STAGE, PACKED, PF, 1>(a, it, lds); break;
     case 2: big_nv_tile<STAGE, PACKED, PF, 2>(a, it, lds); break;
