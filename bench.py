@@ -81,7 +81,12 @@ def gemm_source(workload: str) -> str:
     return "gemm.hip" if small else "gemm_big.hip"
 
 
-GEMM_HEADERS = ("moe_common.h", "launch.h")   # included by both GEMM sources
+# headers each GEMM source includes (a change to any changes its kernels)
+GEMM_HEADERS = {
+    "gemm.hip": ("gemm_tile.h", "moe_common.h", "launch.h"),
+    "gemm_big.hip": ("moe_common.h", "launch.h"),
+    "fused.hip": ("gemm_tile.h", "quant_row.h", "combine.h", "moe_common.h", "launch.h"),
+}
 
 
 def gemm_source_sha256(fname: str) -> str:
@@ -89,20 +94,27 @@ def gemm_source_sha256(fname: str) -> str:
     order: a change to any of them changes the compiled kernel."""
     import hashlib
     h = hashlib.sha256()
-    for f in (fname, *GEMM_HEADERS):
+    for f in (fname, *GEMM_HEADERS[fname]):
         h.update(open(os.path.join(ROOT, "block_scaled_expert_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes (fetch + write) per launch of `kernel` ("gate_up" / "down")
-    recorded from rocprofv3 counters in profiles/traffic.json, if the GEMM
-    source and its headers have not changed since; else None."""
+def fused_applies(T: int, k: int, E: int) -> bool:
+    """moe_forward_fused runs its persistent launch for at most 4096 pairs
+    and at most 48 expected rows per expert (work-list entries of <= 64 rows)."""
+    return T * k <= 4096 and T * k <= 48 * E
+
+
+def measured_traffic(workload: str, kernel: str, fused: bool = False):
+    """HBM bytes (fetch + write) per launch of `kernel` ("gate_up" / "down",
+    or "fused" for the persistent launch) recorded from rocprofv3 counters in
+    profiles/traffic.json, if the kernel source and its headers have not
+    changed since; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(workload)
-    fname = gemm_source(workload)
+    rec = json.load(open(path)).get(workload + ("+fused" if fused else ""))
+    fname = "fused.hip" if fused else gemm_source(workload)
     if (not rec or rec.get("source_file") != fname or rec.get("source_sha256") != gemm_source_sha256(fname)
             or kernel not in rec):
         return None
@@ -208,6 +220,8 @@ def main() -> int:
     ap.add_argument("--encode", choices=["nvfp4", "mxfp8"], default=None,
                     help="instead of the layer: time moe_encode_weights on bf16 experts of the Inkling shape")
     ap.add_argument("--encode-experts", type=int, default=64)
+    ap.add_argument("--fused", action="store_true",
+                    help="moe_forward_fused: the expert half as one persistent launch")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -252,7 +266,7 @@ def main() -> int:
 
     def step(events=None):
         bse.route(cfg, xt, wrt, bt, ids, tw, None, ws)
-        bse.forward(cfg, xt, ids, tw, cw, out, ws, events=events)
+        bse.forward(cfg, xt, ids, tw, cw, out, ws, events=events, fused=args.fused)
 
     for _ in range(args.warmup):
         step()
@@ -331,7 +345,18 @@ def main() -> int:
     decode = w.key.startswith("decode") or w.key == "tiny"
     gemm_kernel = ("k_expert_gemm" if gemm_source(w.key) == "gemm.hip"
                    else "k_expert_gemm_big_nv" if w.fmt == "nvfp4" else "k_expert_gemm_big_mx")
-    if decode or w.key.startswith("ep8"):
+    persistent = args.fused and fused_applies(T, k, E)
+    if persistent:
+        # the persistent launch: both expert GEMMs' weights per launch
+        fb = w13_bytes + w2_bytes + per_expert["gs"]
+        achieved = active * fb / (gate_up_ms * 1e-3) / 1e9
+        tr = measured_traffic(w.key, "fused", fused=True) if args.layout == "packed" else None
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": tr,
+                "traffic_over_algorithmic": None if tr is None else round(tr / (active * fb), 4),
+                "kernel": "k_moe_fused (gate/up, h quantization, down, combine)",
+                "per_launch": f"{active} experts x {fb} B (w13 + w2 codes + scales)"}
+    elif decode or w.key.startswith("ep8"):
         achieved = active * w13_bytes / (gate_up_ms * 1e-3) / 1e9
         tr = measured_traffic(w.key, "gate_up") if args.layout == "packed" else None
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -357,7 +382,8 @@ def main() -> int:
         "data": "synthetic (seeded; expert weights drawn as codes)",
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "ffn": w.ffn,
                    "format": w.fmt, "local_experts": cfg.num_local, "weight_layout": args.layout,
-                   "launch": "hip_graph" if args.graph else "eager",
+                   "launch": ("hip_graph" if args.graph else "eager") + (", persistent expert half" if persistent
+                                                                          else ""),
                    "parallelism": "single GPU"},
         "roofline": roof,
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2),

@@ -3,7 +3,8 @@
 Argument marshalling only: every step of the layer runs in the library's HIP
 kernels on the caller's current torch stream.  The functions mirror the C
 ABI in include/moe.h (moe_route, moe_dispatch, moe_quantize_act,
-moe_forward, moe_workspace_size, moe_check_arch, moe_status_string).
+moe_forward, moe_forward_fused, moe_workspace_size, moe_check_arch,
+moe_status_string).
 Tensors must be contiguous and on the current CUDA (HIP) device; the library
 never allocates, so callers pass outputs and a workspace.
 
@@ -26,7 +27,7 @@ STAGES = ("quant_x", "dispatch", "gate_up", "quant_h", "down", "combine")
 
 EXPORTED = ("moe_status_string", "moe_check_arch", "moe_validate_config", "moe_workspace_size",
             "moe_quantize_act", "moe_route", "moe_dispatch", "moe_prepare_weights", "moe_forward",
-            "moe_encode_weights", "moe_decode_weights")
+            "moe_forward_fused", "moe_encode_weights", "moe_decode_weights")
 LAYOUT_CANONICAL, LAYOUT_PACKED = 0, 1
 
 
@@ -75,6 +76,7 @@ def load() -> ctypes.CDLL:
                                         vp]
     lib.moe_forward.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, ctypes.POINTER(CWeights), vp, vp,
                                 sz, vp, vp]
+    lib.moe_forward_fused.argtypes = lib.moe_forward.argtypes
     for name in EXPORTED:
         if name != "moe_status_string":
             getattr(lib, name).restype = ctypes.c_int
@@ -275,9 +277,10 @@ def prepare_weights(cfg: Config, w: dict) -> dict:
     return out
 
 
-def forward(cfg: Config, x, topk_ids, topk_w, weights, out, ws, events=None) -> None:
+def forward(cfg: Config, x, topk_ids, topk_w, weights, out, ws, events=None, fused: bool = False) -> None:
     """weights: dict of device tensors or a CWeights built by weights_struct.
-    events: optional list of 2*6 torch.cuda.Event (stage timing)."""
+    events: optional list of 2*6 torch.cuda.Event (stage timing).
+    fused: call moe_forward_fused (the persistent launch) instead of moe_forward."""
     import torch
     T = x.shape[0]
     H, k = cfg.hidden, cfg.top_k
@@ -288,8 +291,9 @@ def forward(cfg: Config, x, topk_ids, topk_w, weights, out, ws, events=None) -> 
             raise ValueError("events must hold 2 per stage")
         ev = (ctypes.c_void_p * len(events))(*[e.cuda_event if e is not None else None for e in events])
     cc = cfg.c()
-    _ok(load().moe_forward(ctypes.byref(cc), _ptr(x, torch.bfloat16, (T, H), "x"), T,
-                           _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
-                           _ptr(topk_w, torch.float32, (T, k), "topk_w"), ctypes.byref(cw),
-                           _ptr(out, torch.bfloat16, (T, H), "out"), _ptr(ws, torch.uint8, None, "ws"),
-                           ws.numel(), _stream(), ev), "moe_forward")
+    fn = load().moe_forward_fused if fused else load().moe_forward
+    _ok(fn(ctypes.byref(cc), _ptr(x, torch.bfloat16, (T, H), "x"), T,
+           _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+           _ptr(topk_w, torch.float32, (T, k), "topk_w"), ctypes.byref(cw),
+           _ptr(out, torch.bfloat16, (T, H), "out"), _ptr(ws, torch.uint8, None, "ws"),
+           ws.numel(), _stream(), ev), "moe_forward_fused" if fused else "moe_forward")

@@ -33,7 +33,7 @@ int n_local(const moe_config* c) { return c->num_local_experts; }
 
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct Layout {
-  size_t z, xq, xs, xg, counts, offsets, sorted, pos, work, ntiles, h, hq, hs, hg, y, total;
+  size_t z, xq, xs, xg, counts, offsets, sorted, pos, work, ntiles, ctl, h, hq, hs, hg, y, total;
   int max_tiles, nchunks;
 };
 
@@ -61,6 +61,7 @@ Layout layout(const moe_config* c, int T) {
   L.pos = take(P * 4);
   L.work = take((size_t)L.max_tiles * 2 * 4);
   L.ntiles = take(4);
+  L.ctl = take((size_t)fused_ctl_words(L.max_tiles) * 4);
   L.h = take(nv ? P * F * 4 : 0);    // fp32 h: NVFP4 only (MXFP8 h is encoded by the gate/up epilogue)
   L.hq = take(P * (nv ? F / 2 : F));
   L.hs = take(P * (nv ? F / 16 : F / 32));
@@ -258,9 +259,9 @@ int moe_prepare_weights(const moe_config* c, const moe_expert_weights* src, moe_
   return MOE_OK;
 }
 
-int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* topk_ids, const float* topk_w,
-                const moe_expert_weights* w, void* out, void* ws, size_t ws_bytes, void* stream,
-                void* const* events) {
+static int forward_impl(const moe_config* c, const void* x, int32_t T, const int32_t* topk_ids,
+                        const float* topk_w, const moe_expert_weights* w, void* out, void* ws, size_t ws_bytes,
+                        void* stream, void* const* events, bool fused) {
   int st = moe_validate_config(c);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
@@ -290,13 +291,17 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   b.pos = at<int32_t>(ws, L.pos);
   b.worklist = at<int32_t>(ws, L.work);
   b.ntiles = at<int32_t>(ws, L.ntiles);
+  // the persistent launch covers work-list entries of 16 to 64 rows after
+  // the one-launch quantize + dispatch (which also clears its control words)
+  fused = fused && P <= kSmallDispatchPairs && tile_m <= 64;
   if (P <= kSmallDispatchPairs) {
     // 1 + 2. quantize x per row and dispatch (+ tile list) in one launch; the
     // quantize-x stage covers both, the dispatch stage is empty
     record(events, 2 * MOE_STAGE_QUANT_X, s);
     bad |= launch_prep_small(c->fmt, static_cast<const uint16_t*>(x), T, H, at<uint8_t>(ws, L.xq),
                              at<uint8_t>(ws, L.xs), at<float>(ws, L.xg), topk_ids, P, c->expert_begin, EL, tile_m,
-                             b, s);
+                             b, fused ? at<int32_t>(ws, L.ctl) : nullptr,
+                             fused ? fused_ctl_words(L.max_tiles) : 0, s);
     record(events, 2 * MOE_STAGE_QUANT_X + 1, s);
     record(events, 2 * MOE_STAGE_DISPATCH, s);
     record(events, 2 * MOE_STAGE_DISPATCH + 1, s);
@@ -338,19 +343,8 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   g.out = fuse_h ? nullptr : at<float>(ws, L.h);
   g.out_q = fuse_h ? at<uint8_t>(ws, L.hq) : nullptr;
   g.out_s = fuse_h ? at<uint8_t>(ws, L.hs) : nullptr;
-  record(events, 2 * MOE_STAGE_GATE_UP, s);
-  bad |= launch_gemm_gateup(g, s);
-  record(events, 2 * MOE_STAGE_GATE_UP + 1, s);
 
-  // 4. quantize h per (token, expert) row (NVFP4: the row scale needs the
-  // whole row, so a kernel of its own; the row count lives on the device)
-  record(events, 2 * MOE_STAGE_QUANT_H, s);
-  if (!fuse_h)
-    bad |= launch_quant(c->fmt, 1, at<float>(ws, L.h), P, b.offsets + EL, F, at<uint8_t>(ws, L.hq),
-                        at<uint8_t>(ws, L.hs), at<float>(ws, L.hg), s);
-  record(events, 2 * MOE_STAGE_QUANT_H + 1, s);
-
-  // 5. down GEMM -> y (fp32, sorted rows)
+  // down GEMM arguments
   GemmArgs d = g;
   d.a_codes = at<uint8_t>(ws, L.hq);
   d.a_sc = at<uint8_t>(ws, L.hs);
@@ -364,6 +358,44 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   const size_t y_bytes = (size_t)T * k * EL / c->num_experts * H * sizeof(float);
   const bool stream_y = y_bytes > kStreamBytes;
   d.stream_out = stream_y ? 1 : 0;
+
+  if (fused) {
+    // 3-6 in one persistent launch, timed by the GATE_UP pair
+    FusedArgs f{};
+    f.ctl = at<int32_t>(ws, L.ctl);
+    f.max_tiles = g.max_tiles;
+    f.h = at<float>(ws, L.h);
+    f.hq = at<uint8_t>(ws, L.hq);
+    f.hs = at<uint8_t>(ws, L.hs);
+    f.hg = at<float>(ws, L.hg);
+    f.y = at<float>(ws, L.y);
+    f.pos = b.pos;
+    f.topk_w = topk_w;
+    f.T = T;
+    f.out = static_cast<uint16_t*>(out);
+    record(events, 2 * MOE_STAGE_GATE_UP, s);
+    bad |= launch_moe_fused(g, d, f, s);
+    record(events, 2 * MOE_STAGE_GATE_UP + 1, s);
+    for (int st = MOE_STAGE_QUANT_H; st <= MOE_STAGE_COMBINE; st++) {
+      record(events, 2 * st, s);
+      record(events, 2 * st + 1, s);
+    }
+    return bad ? MOE_ERR_LAUNCH : MOE_OK;
+  }
+
+  record(events, 2 * MOE_STAGE_GATE_UP, s);
+  bad |= launch_gemm_gateup(g, s);
+  record(events, 2 * MOE_STAGE_GATE_UP + 1, s);
+
+  // 4. quantize h per (token, expert) row (NVFP4: the row scale needs the
+  // whole row, so a kernel of its own; the row count lives on the device)
+  record(events, 2 * MOE_STAGE_QUANT_H, s);
+  if (!fuse_h)
+    bad |= launch_quant(c->fmt, 1, at<float>(ws, L.h), P, b.offsets + EL, F, at<uint8_t>(ws, L.hq),
+                        at<uint8_t>(ws, L.hs), at<float>(ws, L.hg), s);
+  record(events, 2 * MOE_STAGE_QUANT_H + 1, s);
+
+  // 5. down GEMM -> y (fp32, sorted rows)
   record(events, 2 * MOE_STAGE_DOWN, s);
   bad |= launch_gemm_down(d, s);
   record(events, 2 * MOE_STAGE_DOWN + 1, s);
@@ -374,6 +406,18 @@ int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* to
   record(events, 2 * MOE_STAGE_COMBINE + 1, s);
   (void)nv;
   return bad ? MOE_ERR_LAUNCH : MOE_OK;
+}
+
+int moe_forward(const moe_config* c, const void* x, int32_t T, const int32_t* topk_ids, const float* topk_w,
+                const moe_expert_weights* w, void* out, void* ws, size_t ws_bytes, void* stream,
+                void* const* events) {
+  return forward_impl(c, x, T, topk_ids, topk_w, w, out, ws, ws_bytes, stream, events, false);
+}
+
+int moe_forward_fused(const moe_config* c, const void* x, int32_t T, const int32_t* topk_ids,
+                      const float* topk_w, const moe_expert_weights* w, void* out, void* ws, size_t ws_bytes,
+                      void* stream, void* const* events) {
+  return forward_impl(c, x, T, topk_ids, topk_w, w, out, ws, ws_bytes, stream, events, true);
 }
 
 }  // extern "C"

@@ -246,8 +246,10 @@ __global__ __launch_bounds__(1024) void k_prep_small(const uint16_t* __restrict_
                                                      int P, int E_begin, int E_local, int tile_m,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
                                                      int32_t* __restrict__ pos, int32_t* __restrict__ worklist,
-                                                     int32_t* __restrict__ ntiles) {
+                                                     int32_t* __restrict__ ntiles, int32_t* __restrict__ zero,
+                                                     int nzero) {
   if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < nzero; i += 1024) zero[i] = 0;
     disp_small_body(ids, P, E_begin, E_local, tile_m, offsets, sorted, pos, worklist, ntiles);
     return;
   }
@@ -266,15 +268,16 @@ __global__ __launch_bounds__(1024) void k_prep_small(const uint16_t* __restrict_
 
 int launch_prep_small(int fmt, const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs, float* xg,
                       const int32_t* ids, int P, int E_begin, int E_local, int tile_m, const DispatchBufs& b,
-                      hipStream_t stream) {
+                      int32_t* zero, int nzero, hipStream_t stream) {
   if (P > kSmallP || T <= 0) return -1;
+  if (zero == nullptr) nzero = 0;
   const dim3 grid(1 + ceil_div(T, 4));
   if (fmt == 1)
     hipLaunchKernelGGL(k_prep_small<1>, grid, dim3(1024), 0, stream, x, T, H, xq, xs, xg, ids, P, E_begin, E_local,
-                       tile_m, b.offsets, b.sorted, b.pos, b.worklist, b.ntiles);
+                       tile_m, b.offsets, b.sorted, b.pos, b.worklist, b.ntiles, zero, nzero);
   else
     hipLaunchKernelGGL(k_prep_small<2>, grid, dim3(1024), 0, stream, x, T, H, xq, xs, xg, ids, P, E_begin, E_local,
-                       tile_m, b.offsets, b.sorted, b.pos, b.worklist, b.ntiles);
+                       tile_m, b.offsets, b.sorted, b.pos, b.worklist, b.ntiles, zero, nzero);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

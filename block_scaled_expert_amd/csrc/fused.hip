@@ -1,0 +1,215 @@
+// The expert half of the layer as one persistent launch (small batches):
+// gate/up GEMM + capped SwiGLU, h quantization, down GEMM and the combine run
+// as work items of a single kernel instead of four launches -- the
+// single-launch fused MoE of the pages (SGLang blog "SGLang and Miles Add
+// Day-0 Support for Inkling 2 Small", "Performance"; SGLang cookbook
+// "Inkling-2-Small" section 2, "MegaMoE": dispatch, the two expert GEMMs
+// and combine in one kernel).
+//
+// Work items, in queue order:
+//   gate/up  (work-list entry, 32 h columns)   entries x F/32
+//   down     (work-list entry, 64 y columns)   entries x H/64
+//   combine  (token, 1024 columns)             T x ceil(H/1024)
+// Workgroups take items from a device counter, a few at a time, in
+// increasing order.  An item waits only for items earlier in the queue:
+//   - the last gate/up item of an entry to finish quantizes the entry's h
+//     rows (NVFP4; MXFP8 h is encoded by each gate/up item) and marks the
+//     entry ready;
+//   - a down item waits for its entry's ready mark;
+//   - combine items wait for the count of finished down items.
+// Every item a wait depends on was taken earlier by a running workgroup, so
+// the queue drains whatever number of workgroups the chip keeps resident;
+// each wait is also bounded (a wait that runs out sets an error word and
+// goes on, so every wave reaches the end).
+//
+// The tile bodies are the ones of the separate GEMM kernels (gemm_tile.h),
+// the h quantization is the NVFP4 row definition (quant_row.h) and the
+// combine the fixed-order sum (combine.h): the output is bit-identical to
+// the four-launch chain.  Cross-XCD visibility: each XCD has its own L2.
+// Results another workgroup reads (h, its codes and scales, y) are stored
+// at device scope (written through, never left dirty in an L2); each wave
+// waits for its stores to complete before the workgroup barrier that
+// precedes the completion count, so the count needs no L2 write-back (a
+// release fence here wrote back the whole L2 per item and cost more than
+// the GEMMs).  A consumer invalidates its stale lines (device-scope
+// acquire) after the count or flag it waits for.
+#include "gemm_tile.h"
+#include "quant_row.h"
+#include "combine.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kCtlHead = 0, kCtlDownDone = 1, kCtlErr = 2, kCtlFixed = 4;
+constexpr int kClaim = 2;                     // items taken per counter update
+constexpr uint32_t kSpinLimit = 1u << 20;     // polls (>= 60 ns each) before a wait gives up
+
+__device__ inline int atomic_add_relaxed(int32_t* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One thread: wait until *p >= target, then acquire (device scope).  A
+// wait that runs out of polls sets *err; once *err is set every wait returns
+// at once, so a broken dependency costs one bounded wait, not one per item.
+__device__ inline void wait_at_least(int32_t* p, int target, int32_t* err) {
+  for (uint32_t it = 0;; it++) {
+    if (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+    if (it >= kSpinLimit) {
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    if ((it & 255) == 255 && __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Workgroup barrier after which every wave's stores have completed (each
+// wave waits for its own; the workgroup barrier alone does not wait for
+// stores): with device-scope stores, the workgroup's results are then
+// visible to every XCD, and one thread's count or flag publishes them.
+__device__ inline void stores_done_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+}
+
+}  // namespace
+
+template <int FMT, int MS, int NSTG, int NSTD, bool PACKED>
+__global__ __launch_bounds__(256, 4) void k_moe_fused(GemmArgs g, GemmArgs d, FusedArgs f) {
+  constexpr int PF = FMT == 1 ? 3 : 2;
+  constexpr int TM = 16 * MS;
+  __shared__ union {
+    TileLds<0, MS> gu;
+    TileLds<1, MS> dn;
+  } sm;
+  __shared__ int s_next, s_last;
+  const int tid = threadIdx.x;
+  int32_t* const ctl = f.ctl;
+  int32_t* const gu_done = ctl + kCtlFixed;
+  int32_t* const ready = ctl + kCtlFixed + f.max_tiles;
+
+  const int nt = g.ntiles[0];   // written by the preceding dispatch launch
+  const int F = g.F, H = g.H;
+  const int nb1 = F / 32, nb2 = H / 64, ncb = (H / 4 + 255) / 256;
+  const int n1 = nt * nb1, n2 = nt * nb2;
+  const int total = n1 + n2 + f.T * ncb;
+
+  if (tid == 0) s_next = atomic_add_relaxed(ctl + kCtlHead, kClaim);
+  __syncthreads();
+  int base = __builtin_amdgcn_readfirstlane(s_next);   // uniform: scalar registers
+  bool downs_seen = false;
+  while (base < total) {
+    __syncthreads();   // every thread has read s_next; the LDS of the last item is free
+    int nxt = 0;
+    if (tid == 0) nxt = atomic_add_relaxed(ctl + kCtlHead, kClaim);   // used after these items
+    const int end = min(base + kClaim, total);
+    for (int item = base; item < end; item++) {
+      // the thread index, opaque to the compiler: nothing derived from it is
+      // hoisted out of the item loop and kept live across items
+      int tix = tid;
+      asm volatile("" : "+v"(tix));
+      if (item < n1) {
+        // gate/up + capped SwiGLU (MXFP8: h encoded here)
+        const int tile = item / nb1, bx = item - tile * nb1;
+        expert_tile<FMT, 0, MS, PF, NSTG, PACKED, true>(g, tile, bx, sm.gu, tix);
+        stores_done_barrier();
+        if (tid == 0) {
+          const bool last =
+              __hip_atomic_fetch_add(gu_done + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nb1 - 1;
+          if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other items' h
+          s_last = last;
+        }
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(s_last)) {
+          if constexpr (FMT == 1) {
+            // the entry's h rows are complete: quantize them, one row per wave
+            const int el = g.worklist[2 * tile], m0 = g.worklist[2 * tile + 1];
+            const int row0 = g.offsets[el] + m0;
+            const int rows = min(TM, g.offsets[el + 1] - row0);
+            const int wave = tid >> 6, lane = tid & 63;
+            for (int m = wave; m < rows; m += 4) {
+              const size_t r = (size_t)(row0 + m);
+              quant_row_nvfp4_wave<float>(f.h + r * F, F, lane, f.hq + r * (F / 2), f.hs + r * (F / 16),
+                                          f.hg + r);
+            }
+            stores_done_barrier();
+          }
+          if (tid == 0) __hip_atomic_store(ready + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      } else if (item < n1 + n2) {
+        const int i2 = item - n1, tile = i2 / nb2, bx = i2 - tile * nb2;
+        if (tid == 0) wait_at_least(ready + tile, 1, ctl + kCtlErr);
+        __syncthreads();
+        expert_tile<FMT, 1, MS, PF, NSTD, PACKED, true>(d, tile, bx, sm.dn, tix);
+        stores_done_barrier();
+        if (tid == 0) atomic_add_relaxed(ctl + kCtlDownDone, 1);
+      } else {
+        const int i3 = item - n1 - n2, t = i3 / ncb, cb = i3 - t * ncb;
+        if (!downs_seen) {
+          if (tid == 0) wait_at_least(ctl + kCtlDownDone, n2, ctl + kCtlErr);
+          __syncthreads();
+          downs_seen = true;
+        }
+        const int c = cb * 256 + tid;
+        if (c < H / 4) combine_col4<false>(f.y, f.pos, f.topk_w, g.k, H, f.out, t, c);
+      }
+    }
+    if (tid == 0) s_next = nxt;
+    __syncthreads();
+    base = __builtin_amdgcn_readfirstlane(s_next);
+  }
+}
+
+int fused_ctl_words(int max_tiles) { return kCtlFixed + 2 * max_tiles; }
+
+namespace {
+
+template <int FMT, int MS, int NSTG, int NSTD, bool PACKED>
+int launch_fused_t(const GemmArgs& g, const GemmArgs& d, const FusedArgs& f, hipStream_t stream) {
+  // as many workgroups as stay resident (more would only take no item)
+  static int resident[2] = {0, 0};   // per-kernel cache: [0] per-CU blocks, [1] CUs
+  if (resident[0] == 0) {
+    int dev = 0, per_cu = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_moe_fused<FMT, MS, NSTG, NSTD, PACKED>, 256, 0) !=
+        hipSuccess)
+      return -1;
+    resident[1] = cus;
+    resident[0] = per_cu > 0 ? per_cu : 1;
+  }
+  const dim3 grid(resident[0] * resident[1]);
+  hipLaunchKernelGGL((k_moe_fused<FMT, MS, NSTG, NSTD, PACKED>), grid, dim3(256), 0, stream, g, d, f);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int FMT, int MS>
+int launch_fused_ms(const GemmArgs& g, const GemmArgs& d, const FusedArgs& f, hipStream_t stream) {
+  // Inkling 2 Small: H = 4608 gives 36 k steps = 4 waves x 9 (gate/up);
+  // F = 2304 gives 18 = 2 waves x 9 (down)
+  const bool fast = g.H == 128 * 9 * 4 && g.F == 128 * 9 * 2;
+  if (g.packed) return fast ? launch_fused_t<FMT, MS, 9, 9, true>(g, d, f, stream)
+                            : launch_fused_t<FMT, MS, 0, 0, true>(g, d, f, stream);
+  return fast ? launch_fused_t<FMT, MS, 9, 9, false>(g, d, f, stream)
+              : launch_fused_t<FMT, MS, 0, 0, false>(g, d, f, stream);
+}
+
+}  // namespace
+
+int launch_moe_fused(const GemmArgs& g, const GemmArgs& d, const FusedArgs& f, hipStream_t stream) {
+  const int ms = g.tile_m / 16;
+  if (g.fmt == 1) {
+    if (ms == 1) return launch_fused_ms<1, 1>(g, d, f, stream);
+    if (ms == 2) return launch_fused_ms<1, 2>(g, d, f, stream);
+    if (ms == 4) return launch_fused_ms<1, 4>(g, d, f, stream);
+  } else {
+    if (ms == 1) return launch_fused_ms<2, 1>(g, d, f, stream);
+    if (ms == 2) return launch_fused_ms<2, 2>(g, d, f, stream);
+    if (ms == 4) return launch_fused_ms<2, 4>(g, d, f, stream);
+  }
+  return -1;
+}
+
+}  // namespace moe

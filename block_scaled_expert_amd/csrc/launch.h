@@ -41,9 +41,10 @@ int launch_dispatch(const int32_t* ids, int P, int E_begin, int E_local, int til
 constexpr int kSmallDispatchPairs = 4096;
 // ... and can share a launch with the quantization of the bf16 token rows
 // (xq / xs / xg as launch_quant writes them for fmt 1 or 2).
+// zero (nullable): nzero int32 words the launch also clears.
 int launch_prep_small(int fmt, const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs, float* xg,
                       const int32_t* ids, int P, int E_begin, int E_local, int tile_m, const DispatchBufs& b,
-                      hipStream_t stream);
+                      int32_t* zero, int nzero, hipStream_t stream);
 
 // Weight encoding: nmat matrices [rows][cols] (dtype 0 bf16, 1 fp32) to
 // canonical NVFP4 (fmt 1: one fp32 scale per matrix, written to
@@ -99,6 +100,27 @@ bool gemm_big_supported(int H, int F);
 int launch_gemm_big(const GemmArgs& a, int stage, hipStream_t stream);
 int launch_gemm_gateup(const GemmArgs& a, hipStream_t stream);
 int launch_gemm_down(const GemmArgs& a, hipStream_t stream);
+
+// The expert half as one persistent launch (fused.hip) for work-list entries
+// of 16 to 64 rows.  ctl: fused_ctl_words(max_tiles) int32 words, zero when
+// the launch starts (the quantize + dispatch launch before it clears them).
+struct FusedArgs {
+  int32_t* ctl;
+  int max_tiles;
+  // NVFP4 h quantization per sorted row: fp32 h in; codes, scales, row scales out
+  const float* h;
+  uint8_t* hq;
+  uint8_t* hs;
+  float* hg;
+  // combine
+  const float* y;
+  const int32_t* pos;
+  const float* topk_w;
+  int T;
+  uint16_t* out;
+};
+int fused_ctl_words(int max_tiles);
+int launch_moe_fused(const GemmArgs& g, const GemmArgs& d, const FusedArgs& f, hipStream_t stream);
 
 // Repack nmat canonical [N][K] matrices (codes + scales) into the packed
 // tile layout (moe_prepare_weights).

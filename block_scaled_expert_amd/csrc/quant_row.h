@@ -53,6 +53,33 @@ __device__ inline float group_max(float v, float* red, int t) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// One NVFP4 block of 16 values of a row with fp32 scale gs (denom = 6 gs):
+// returns its E4M3 scale byte, codes in w0 (values 0-7) and w1 (8-15).
+__device__ inline uint32_t nvfp4_block(const float* v, float gs, float denom, bool zero_row, uint32_t& w0,
+                                       uint32_t& w1) {
+#pragma clang fp contract(off)
+  float ab = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; i++) ab = fmaxf(ab, fabsf(v[i]));
+  uint32_t sc = e4m3_hw(__fdiv_rn(ab, denom));
+  const float sigma = e4m3_decode(sc);
+  w0 = 0;
+  w1 = 0;
+  if (!zero_row && sigma != 0.0f) {
+    const float r = __fdiv_rn(1.0f, __fmul_rn(sigma, gs));
+    if (r <= 3.4028235e38f) {   // r overflows only where the row (or matrix) maximum is below ~4e-33
+      w0 = e2m1_pack8(v, r);
+      w1 = e2m1_pack8(v + 8, r);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; i++) w0 |= e2m1_encode(__fmul_rn(v[i], r)) << (4 * i);
+#pragma unroll
+      for (int i = 0; i < 8; i++) w1 |= e2m1_encode(__fmul_rn(v[8 + i], r)) << (4 * i);
+    }
+  }
+  return zero_row ? 0u : sc;
+}
+
 // NVFP4 row of `cols` elements: codes (cols/2 bytes), E4M3 block scales
 // (cols/16) and the fp32 row scale.  live == false: the row is read and the
 // barrier taken, nothing is written.
@@ -78,29 +105,45 @@ __device__ inline void quant_row_nvfp4(const InT* __restrict__ xr, int cols, int
   for (int b = t; b < nblk; b += 256) {
     float v[16];
     load_block<InT>(xr + 16 * b, 16, v);
-    float ab = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i++) ab = fmaxf(ab, fabsf(v[i]));
-    uint32_t sc = e4m3_hw(__fdiv_rn(ab, denom));
-    const float sigma = e4m3_decode(sc);
-    uint32_t w0 = 0, w1 = 0;
-    if (!zero_row && sigma != 0.0f) {
-      const float r = __fdiv_rn(1.0f, __fmul_rn(sigma, gs));
-      if (r <= 3.4028235e38f) {   // r overflows only where the row (or matrix) maximum is below ~4e-33
-        w0 = e2m1_pack8(v, r);
-        w1 = e2m1_pack8(v + 8, r);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; i++) w0 |= e2m1_encode(__fmul_rn(v[i], r)) << (4 * i);
-#pragma unroll
-        for (int i = 0; i < 8; i++) w1 |= e2m1_encode(__fmul_rn(v[8 + i], r)) << (4 * i);
-      }
-    }
-    if (zero_row) sc = 0;
+    uint32_t w0, w1;
+    const uint32_t sc = nvfp4_block(v, gs, denom, zero_row, w0, w1);
     if (live) {
       *reinterpret_cast<uint2*>(cr + 8 * b) = make_uint2(w0, w1);
       sr[b] = (uint8_t)sc;
     }
+  }
+}
+
+// The same NVFP4 row quantization by one wave (64 lanes, lane index t) with
+// no workgroup barrier: several rows quantize side by side, one per wave.
+// Outputs are device-scope stores (written through for readers on other
+// XCDs).
+template <typename InT>
+__device__ inline void quant_row_nvfp4_wave(const InT* __restrict__ xr, int cols, int t,
+                                            uint8_t* __restrict__ cr, uint8_t* __restrict__ sr,
+                                            float* __restrict__ gs_out) {
+#pragma clang fp contract(off)
+  const int nblk = cols / 16;
+  float A = 0.0f;
+  for (int b = t; b < nblk; b += 64) {
+    float v[16];
+    load_block<InT>(xr + 16 * b, 16, v);
+#pragma unroll
+    for (int i = 0; i < 16; i++) A = fmaxf(A, fabsf(v[i]));
+  }
+  A = wave_max(A);
+  const bool zero_row = (A == 0.0f);
+  const float gs = zero_row ? 1.0f : __fdiv_rn(A, 2688.0f);
+  const float denom = __fmul_rn(6.0f, gs);
+  if (t == 0) __hip_atomic_store(gs_out, gs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int b = t; b < nblk; b += 64) {
+    float v[16];
+    load_block<InT>(xr + 16 * b, 16, v);
+    uint32_t w0, w1;
+    const uint32_t sc = nvfp4_block(v, gs, denom, zero_row, w0, w1);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(cr + 8 * b), (uint64_t)w0 | ((uint64_t)w1 << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(sr + b, (uint8_t)sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -17,7 +17,7 @@ from _util import OUT_RTOL, inputs, lib_cfg, oracle_cfg, rel_err, stack_local, t
 pytestmark = pytest.mark.gpu
 
 
-def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None, layout="packed"):
+def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None, layout="packed", fused=False):
     import torch
     x, wr, b = inputs(w, T)
     T = x.shape[0]
@@ -35,7 +35,7 @@ def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None, layout="
     wrt = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).cuda()
     out = torch.empty((T, w.hidden), dtype=torch.bfloat16, device="cuda")
     bse.route(cfg, xt, wrt, torch.from_numpy(b).cuda(), ids, tw, nt, ws)
-    bse.forward(cfg, xt, ids, tw, wd, out, ws)
+    bse.forward(cfg, xt, ids, tw, wd, out, ws, fused=fused)
     torch.cuda.synchronize()
     return dict(x=x, wr=wr, b=b, ids=ids.cpu().numpy(), tw=tw.cpu().numpy(),
                 out=out.view(torch.int16).cpu().numpy().view(np.uint16), ews=ews)

@@ -1,0 +1,100 @@
+"""moe_forward_fused (the persistent single-launch expert half) on the GPU.
+
+Its work items run the same tile bodies, the same h quantization and the
+same fixed-order combine as moe_forward's launch sequence, so the two
+outputs must be bit-identical; each is also held to the oracle's bar
+(max|gpu - oracle| / max|oracle| <= 2e-2, routing replayed).  Shapes cover
+all three work-list entry heights the persistent launch serves (16, 32 and
+64 rows), both formats and weight layouts, EP shares (partial sums), a
+single token, Inkling-size decode batches, repeated calls on one workspace
+(the control words are cleared by each call's dispatch launch) and a batch
+outside its range (128-row entries: moe_forward's launch sequence runs).
+"""
+import numpy as np
+import pytest
+
+import synth
+
+from _util import OUT_RTOL, rel_err
+from test_gpu_forward import SMALL, oracle_out, run_layer
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # expected rows per local expert <= 2: 16-row entries
+    "tiny": synth.WORKLOADS["tiny"],
+    # 4..24: 32-row entries
+    "mid_nvfp4": SMALL["mid_nvfp4"],
+    "mid_mxfp8": SMALL["mid_mxfp8"],
+    "ep_nvfp4": SMALL["ep_nvfp4"],
+    "ep_mxfp8": SMALL["ep_mxfp8"],
+    # 24..48: 64-row entries
+    "rows64_nvfp4": synth.Workload("rows64_nvfp4", "64-row entries", 256, 512, 32, 4, 256, "nvfp4", 41,
+                                   weights="gaussian"),
+    "rows64_mxfp8": synth.Workload("rows64_mxfp8", "64-row entries", 240, 256, 24, 4, 256, "mxfp8", 42,
+                                   weights="gaussian"),
+    # skewed loads: many experts with one entry, a few with several
+    "zipf_nvfp4": synth.Workload("zipf_nvfp4", "skewed", 96, 512, 64, 6, 256, "nvfp4", 43, bias="zipf",
+                                 weights="gaussian"),
+    # 128-row entries: outside the persistent launch's range
+    "many_rows": SMALL["many_rows"],
+}
+
+
+@pytest.mark.parametrize("key", list(CASES))
+def test_fused_matches_launch_sequence_and_oracle(gpu_lib, key):
+    w = CASES[key]
+    a = run_layer(gpu_lib, w)
+    b = run_layer(gpu_lib, w, fused=True)
+    assert np.array_equal(a["ids"], b["ids"])
+    assert np.array_equal(a["out"], b["out"])
+    assert rel_err(b["out"], oracle_out(w, b)) <= OUT_RTOL
+
+
+@pytest.mark.parametrize("layout", ["canonical", "packed"])
+def test_fused_single_token(gpu_lib, layout):
+    w = SMALL["mid_mxfp8"]
+    a = run_layer(gpu_lib, w, T=1, max_tokens=200, layout=layout)
+    b = run_layer(gpu_lib, w, T=1, max_tokens=200, layout=layout, fused=True)
+    assert np.array_equal(a["out"], b["out"])
+    assert rel_err(b["out"], oracle_out(w, b)) <= OUT_RTOL
+
+
+@pytest.mark.parametrize("key", ["decode_nvfp4", "decode_mxfp8"])
+def test_fused_inkling_decode_bit_exact(gpu_lib, key):
+    """Inkling-size decode batches: bit-identical to moe_forward on every
+    token, and sampled tokens against the oracle."""
+    w = synth.WORKLOADS[key]
+    a = run_layer(gpu_lib, w)
+    b = run_layer(gpu_lib, w, fused=True)
+    assert np.array_equal(a["out"], b["out"])
+    b["ews"] = None
+    toks = np.random.default_rng(2).choice(w.tokens, 2, replace=False)
+    assert rel_err(b["out"][toks], oracle_out(w, b, tokens=toks)) <= OUT_RTOL
+
+
+def test_fused_repeated_calls_one_workspace(gpu_lib):
+    """Several calls on one workspace, with batches of different sizes: each
+    call's dispatch launch clears the queue and counters the last one left."""
+    import torch
+    from _util import inputs, lib_cfg, stack_local, to_dev
+    bse = gpu_lib
+    w = SMALL["mid_nvfp4"]
+    cfg = lib_cfg(bse, w, max_tokens=w.tokens)
+    stacked, _ = stack_local(w)
+    wd = bse.prepare_weights(cfg, {k: to_dev(v) for k, v in stacked.items()})
+    ws = bse.workspace(cfg)
+    x, wr, b = inputs(w, w.tokens)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    wrt = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).cuda()
+    bt = torch.from_numpy(b).cuda()
+    for T in (w.tokens, 7, w.tokens, 1, 33):
+        ids = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
+        ref = torch.empty((T, w.hidden), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty_like(ref)
+        bse.route(cfg, xt[:T], wrt, bt, ids, tw, None, ws)
+        bse.forward(cfg, xt[:T], ids, tw, wd, ref, ws)
+        bse.forward(cfg, xt[:T], ids, tw, wd, out, ws, fused=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), T
