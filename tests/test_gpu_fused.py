@@ -98,3 +98,15 @@ def test_fused_repeated_calls_one_workspace(gpu_lib):
         bse.forward(cfg, xt[:T], ids, tw, wd, out, ws, fused=True)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), T
+
+
+@pytest.mark.parametrize("form", [0, 1, 2, 3])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+def test_fused_cap_forms_under_stress(gpu_lib, form, fmt):
+    """Expert weights x10 so gate/up values pass the cap: every capped-SwiGLU
+    form in the persistent launch's gate/up items."""
+    w = synth.Workload("cap", "cap stress", 48, 512, 16, 4, 256, fmt, 27, weights="gaussian")
+    a = run_layer(gpu_lib, w, gain=10.0, cap_form=form)
+    b = run_layer(gpu_lib, w, gain=10.0, cap_form=form, fused=True)
+    assert np.array_equal(a["out"], b["out"])
+    assert rel_err(b["out"], oracle_out(w, b, cap_form=form)) <= OUT_RTOL
