@@ -280,7 +280,11 @@ int moe_forward(const moe_config* cfg, const void* x, int32_t T, const int32_t* 
  * "MegaMoE").  After the one-launch x quantization + dispatch, one kernel
  * runs gate/up + capped SwiGLU, h quantization, down and the combine as
  * work items taken from a device-side queue; an item waits only on items
- * before it in the queue, each wait is bounded.  Same arguments, workspace,
+ * before it in the queue, so the queue drains whatever the number of
+ * resident workgroups.  Each wait is also bounded (about a second of
+ * polling; reaching the bound needs a device fault elsewhere): a wait that
+ * runs out sets an error word in the workspace, every later wait returns at
+ * once, the launch completes and `out` is undefined.  Same arguments, workspace,
  * result (bit-identical to moe_forward) and errors as moe_forward.  It
  * applies when T * top_k <= 4096 and the expected rows per local expert
  * (T * top_k / num_experts) are at most 48; other batches run moe_forward's
