@@ -10,8 +10,7 @@
 //   gate/up  (work-list entry, 32 h columns)   entries x F/32
 //   down     (work-list entry, 64 y columns)   entries x H/64
 //   combine  (token, 1024 columns)             T x ceil(H/1024)
-// Workgroups take items from a device counter, a few at a time, in
-// increasing order.  An item waits only for items earlier in the queue:
+// Workgroups take items from a device counter in increasing order.  An item waits only for items earlier in the queue:
 //   - the last gate/up item of an entry to finish quantizes the entry's h
 //     rows (NVFP4; MXFP8 h is encoded by each gate/up item) and marks the
 //     entry ready;
@@ -42,7 +41,7 @@ namespace moe {
 namespace {
 
 constexpr int kCtlHead = 0, kCtlDownDone = 1, kCtlErr = 2, kCtlFixed = 4;
-constexpr int kClaim = 2;                     // items taken per counter update
+constexpr int kClaim = 1;   // items per counter update (2 left half the workgroups idle at 1 token)
 constexpr uint32_t kSpinLimit = 1u << 20;     // polls (>= 60 ns each) before a wait gives up
 
 __device__ inline int atomic_add_relaxed(int32_t* p, int v) {
