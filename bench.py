@@ -100,14 +100,14 @@ def gemm_source_sha256(fname: str) -> str:
 
 
 def fused_applies(T: int, k: int, E: int) -> bool:
-    """moe_forward_fused runs its persistent launch for at most 4096 pairs
+    """moe_forward_fused runs its single expert-half launch for at most 4096 pairs
     and at most 48 expected rows per expert (work-list entries of <= 64 rows)."""
     return T * k <= 4096 and T * k <= 48 * E
 
 
 def measured_traffic(workload: str, kernel: str, fused: bool = False):
     """HBM bytes (fetch + write) per launch of `kernel` ("gate_up" / "down",
-    or "fused" for the persistent launch) recorded from rocprofv3 counters in
+    or "fused" for the single expert-half launch) recorded from rocprofv3 counters in
     profiles/traffic.json, if the kernel source and its headers have not
     changed since; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -221,7 +221,7 @@ def main() -> int:
                     help="instead of the layer: time moe_encode_weights on bf16 experts of the Inkling shape")
     ap.add_argument("--encode-experts", type=int, default=64)
     ap.add_argument("--fused", action="store_true",
-                    help="moe_forward_fused: the expert half as one persistent launch")
+                    help="moe_forward_fused: the expert half as one launch")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -345,9 +345,9 @@ def main() -> int:
     decode = w.key.startswith("decode") or w.key == "tiny"
     gemm_kernel = ("k_expert_gemm" if gemm_source(w.key) == "gemm.hip"
                    else "k_expert_gemm_big_nv" if w.fmt == "nvfp4" else "k_expert_gemm_big_mx")
-    persistent = args.fused and fused_applies(T, k, E)
-    if persistent:
-        # the persistent launch: both expert GEMMs' weights per launch
+    single = args.fused and fused_applies(T, k, E)
+    if single:
+        # the single launch: both expert GEMMs. weights per launch
         fb = w13_bytes + w2_bytes + per_expert["gs"]
         achieved = active * fb / (gate_up_ms * 1e-3) / 1e9
         tr = measured_traffic(w.key, "fused", fused=True) if args.layout == "packed" else None
@@ -382,7 +382,7 @@ def main() -> int:
         "data": "synthetic (seeded; expert weights drawn as codes)",
         "config": {"workload": w.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "ffn": w.ffn,
                    "format": w.fmt, "local_experts": cfg.num_local, "weight_layout": args.layout,
-                   "launch": ("hip_graph" if args.graph else "eager") + (", persistent expert half" if persistent
+                   "launch": ("hip_graph" if args.graph else "eager") + (", single-launch expert half" if single
                                                                           else ""),
                    "parallelism": "single GPU"},
         "roofline": roof,

@@ -280,7 +280,7 @@ def prepare_weights(cfg: Config, w: dict) -> dict:
 def forward(cfg: Config, x, topk_ids, topk_w, weights, out, ws, events=None, fused: bool = False) -> None:
     """weights: dict of device tensors or a CWeights built by weights_struct.
     events: optional list of 2*6 torch.cuda.Event (stage timing).
-    fused: call moe_forward_fused (the persistent launch) instead of moe_forward."""
+    fused: call moe_forward_fused (the expert half in one launch) instead of moe_forward."""
     import torch
     T = x.shape[0]
     H, k = cfg.hidden, cfg.top_k

@@ -291,7 +291,7 @@ static int forward_impl(const moe_config* c, const void* x, int32_t T, const int
   b.pos = at<int32_t>(ws, L.pos);
   b.worklist = at<int32_t>(ws, L.work);
   b.ntiles = at<int32_t>(ws, L.ntiles);
-  // the persistent launch covers work-list entries of 16 to 64 rows after
+  // the single launch covers work-list entries of 16 to 64 rows after
   // the one-launch quantize + dispatch (which also clears its control words)
   fused = fused && P <= kSmallDispatchPairs && tile_m <= 64;
   if (P <= kSmallDispatchPairs) {
@@ -360,7 +360,7 @@ static int forward_impl(const moe_config* c, const void* x, int32_t T, const int
   d.stream_out = stream_y ? 1 : 0;
 
   if (fused) {
-    // 3-6 in one persistent launch, timed by the GATE_UP pair
+    // 3-6 in one launch, timed by the GATE_UP pair
     FusedArgs f{};
     f.ctl = at<int32_t>(ws, L.ctl);
     f.max_tiles = g.max_tiles;

@@ -1,25 +1,28 @@
-// The expert half of the layer as one persistent launch (small batches):
-// gate/up GEMM + capped SwiGLU, h quantization, down GEMM and the combine run
-// as work items of a single kernel instead of four launches -- the
-// single-launch fused MoE of the pages (SGLang blog "SGLang and Miles Add
-// Day-0 Support for Inkling 2 Small", "Performance"; SGLang cookbook
-// "Inkling-2-Small" section 2, "MegaMoE": dispatch, the two expert GEMMs
-// and combine in one kernel).
+// The expert half of the layer as one launch (small batches): gate/up GEMM +
+// capped SwiGLU, h quantization, down GEMM and the combine run as work items
+// of a single kernel instead of four launches -- the single-launch fused MoE
+// of the pages (SGLang blog "SGLang and Miles Add Day-0 Support for Inkling 2
+// Small", "Performance"; SGLang cookbook "Inkling-2-Small" section 2,
+// "MegaMoE": dispatch, the two expert GEMMs and combine in one kernel).
 //
 // Work items, in queue order:
 //   gate/up  (work-list entry, 32 h columns)   entries x F/32
 //   down     (work-list entry, 64 y columns)   entries x H/64
 //   combine  (token, 1024 columns)             T x ceil(H/1024)
-// Workgroups take items from a device counter in increasing order.  An item waits only for items earlier in the queue:
+// One workgroup per item: each takes the next item index from a device
+// counter when it starts.  An item waits only for items earlier in the queue:
 //   - the last gate/up item of an entry to finish quantizes the entry's h
 //     rows (NVFP4; MXFP8 h is encoded by each gate/up item) and marks the
 //     entry ready;
 //   - a down item waits for its entry's ready mark;
 //   - combine items wait for the count of finished down items.
 // Every item a wait depends on was taken earlier by a running workgroup, so
-// the queue drains whatever number of workgroups the chip keeps resident;
+// the launch drains whatever number of workgroups the chip keeps resident;
 // each wait is also bounded (a wait that runs out sets an error word and
-// goes on, so every wave reaches the end).
+// goes on, so every wave reaches the end).  (A persistent grid of resident
+// workgroups looping over the items was slower: it drains its loads between
+// items and claims unevenly across CUs, where the hardware dispatcher
+// spreads a grid and overlaps one workgroup's end with the next one's start.)
 //
 // The tile bodies are the ones of the separate GEMM kernels (gemm_tile.h),
 // the h quantization is the NVFP4 row definition (quant_row.h) and the
@@ -41,7 +44,6 @@ namespace moe {
 namespace {
 
 constexpr int kCtlHead = 0, kCtlDownDone = 1, kCtlErr = 2, kCtlFixed = 4;
-constexpr int kClaim = 1;   // items per counter update (2 left half the workgroups idle at 1 token)
 constexpr uint32_t kSpinLimit = 1u << 20;     // polls (>= 60 ns each) before a wait gives up
 
 __device__ inline int atomic_add_relaxed(int32_t* p, int v) {
@@ -75,15 +77,20 @@ __device__ inline void stores_done_barrier() {
 
 }  // namespace
 
+// One workgroup per work item.  The grid covers the largest item count the
+// launch can have; workgroups past the device-side count exit at once, the
+// others take the next item index from the counter when they start.  The
+// hardware dispatches them as slots free up, spread over the CUs, and
+// overlaps one workgroup's end with the next one's start.
 template <int FMT, int MS, int NSTG, int NSTD, bool PACKED>
-__global__ __launch_bounds__(256, 4) void k_moe_fused(GemmArgs g, GemmArgs d, FusedArgs f) {
+__global__ __launch_bounds__(256) void k_moe_fused(GemmArgs g, GemmArgs d, FusedArgs f) {
   constexpr int PF = FMT == 1 ? 3 : 2;
   constexpr int TM = 16 * MS;
   __shared__ union {
     TileLds<0, MS> gu;
     TileLds<1, MS> dn;
   } sm;
-  __shared__ int s_next, s_last;
+  __shared__ int s_item, s_last;
   const int tid = threadIdx.x;
   int32_t* const ctl = f.ctl;
   int32_t* const gu_done = ctl + kCtlFixed;
@@ -94,70 +101,51 @@ __global__ __launch_bounds__(256, 4) void k_moe_fused(GemmArgs g, GemmArgs d, Fu
   const int nb1 = F / 32, nb2 = H / 64, ncb = (H / 4 + 255) / 256;
   const int n1 = nt * nb1, n2 = nt * nb2;
   const int total = n1 + n2 + f.T * ncb;
+  if ((int)blockIdx.x >= total) return;   // exactly `total` workgroups take an item
 
-  if (tid == 0) s_next = atomic_add_relaxed(ctl + kCtlHead, kClaim);
+  if (tid == 0) s_item = atomic_add_relaxed(ctl + kCtlHead, 1);
   __syncthreads();
-  int base = __builtin_amdgcn_readfirstlane(s_next);   // uniform: scalar registers
-  bool downs_seen = false;
-  while (base < total) {
-    __syncthreads();   // every thread has read s_next; the LDS of the last item is free
-    int nxt = 0;
-    if (tid == 0) nxt = atomic_add_relaxed(ctl + kCtlHead, kClaim);   // used after these items
-    const int end = min(base + kClaim, total);
-    for (int item = base; item < end; item++) {
-      // the thread index, opaque to the compiler: nothing derived from it is
-      // hoisted out of the item loop and kept live across items
-      int tix = tid;
-      asm volatile("" : "+v"(tix));
-      if (item < n1) {
-        // gate/up + capped SwiGLU (MXFP8: h encoded here)
-        const int tile = item / nb1, bx = item - tile * nb1;
-        expert_tile<FMT, 0, MS, PF, NSTG, PACKED, true>(g, tile, bx, sm.gu, tix);
-        stores_done_barrier();
-        if (tid == 0) {
-          const bool last =
-              __hip_atomic_fetch_add(gu_done + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nb1 - 1;
-          if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other items' h
-          s_last = last;
-        }
-        __syncthreads();
-        if (__builtin_amdgcn_readfirstlane(s_last)) {
-          if constexpr (FMT == 1) {
-            // the entry's h rows are complete: quantize them, one row per wave
-            const int el = g.worklist[2 * tile], m0 = g.worklist[2 * tile + 1];
-            const int row0 = g.offsets[el] + m0;
-            const int rows = min(TM, g.offsets[el + 1] - row0);
-            const int wave = tid >> 6, lane = tid & 63;
-            for (int m = wave; m < rows; m += 4) {
-              const size_t r = (size_t)(row0 + m);
-              quant_row_nvfp4_wave<float>(f.h + r * F, F, lane, f.hq + r * (F / 2), f.hs + r * (F / 16),
-                                          f.hg + r);
-            }
-            stores_done_barrier();
-          }
-          if (tid == 0) __hip_atomic_store(ready + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      } else if (item < n1 + n2) {
-        const int i2 = item - n1, tile = i2 / nb2, bx = i2 - tile * nb2;
-        if (tid == 0) wait_at_least(ready + tile, 1, ctl + kCtlErr);
-        __syncthreads();
-        expert_tile<FMT, 1, MS, PF, NSTD, PACKED, true>(d, tile, bx, sm.dn, tix);
-        stores_done_barrier();
-        if (tid == 0) atomic_add_relaxed(ctl + kCtlDownDone, 1);
-      } else {
-        const int i3 = item - n1 - n2, t = i3 / ncb, cb = i3 - t * ncb;
-        if (!downs_seen) {
-          if (tid == 0) wait_at_least(ctl + kCtlDownDone, n2, ctl + kCtlErr);
-          __syncthreads();
-          downs_seen = true;
-        }
-        const int c = cb * 256 + tid;
-        if (c < H / 4) combine_col4<false>(f.y, f.pos, f.topk_w, g.k, H, f.out, t, c);
-      }
+  const int item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar registers
+  if (item < n1) {
+    // gate/up + capped SwiGLU (MXFP8: h encoded here)
+    const int tile = item / nb1, bx = item - tile * nb1;
+    expert_tile<FMT, 0, MS, PF, NSTG, PACKED, true>(g, tile, bx, sm.gu, tid);
+    stores_done_barrier();
+    if (tid == 0) {
+      const bool last =
+          __hip_atomic_fetch_add(gu_done + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nb1 - 1;
+      if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the other items' h
+      s_last = last;
     }
-    if (tid == 0) s_next = nxt;
     __syncthreads();
-    base = __builtin_amdgcn_readfirstlane(s_next);
+    if (__builtin_amdgcn_readfirstlane(s_last)) {
+      if constexpr (FMT == 1) {
+        // the entry's h rows are complete: quantize them, one row per wave
+        const int el = g.worklist[2 * tile], m0 = g.worklist[2 * tile + 1];
+        const int row0 = g.offsets[el] + m0;
+        const int rows = min(TM, g.offsets[el + 1] - row0);
+        const int wave = tid >> 6, lane = tid & 63;
+        for (int m = wave; m < rows; m += 4) {
+          const size_t r = (size_t)(row0 + m);
+          quant_row_nvfp4_wave<float>(f.h + r * F, F, lane, f.hq + r * (F / 2), f.hs + r * (F / 16), f.hg + r);
+        }
+        stores_done_barrier();
+      }
+      if (tid == 0) __hip_atomic_store(ready + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if (item < n1 + n2) {
+    const int i2 = item - n1, tile = i2 / nb2, bx = i2 - tile * nb2;
+    if (tid == 0) wait_at_least(ready + tile, 1, ctl + kCtlErr);
+    __syncthreads();
+    expert_tile<FMT, 1, MS, PF, NSTD, PACKED, true>(d, tile, bx, sm.dn, tid);
+    stores_done_barrier();
+    if (tid == 0) atomic_add_relaxed(ctl + kCtlDownDone, 1);
+  } else {
+    const int i3 = item - n1 - n2, t = i3 / ncb, cb = i3 - t * ncb;
+    if (tid == 0) wait_at_least(ctl + kCtlDownDone, n2, ctl + kCtlErr);
+    __syncthreads();
+    const int c = cb * 256 + tid;
+    if (c < H / 4) combine_col4<false>(f.y, f.pos, f.topk_w, g.k, H, f.out, t, c);
   }
 }
 
@@ -167,20 +155,10 @@ namespace {
 
 template <int FMT, int MS, int NSTG, int NSTD, bool PACKED>
 int launch_fused_t(const GemmArgs& g, const GemmArgs& d, const FusedArgs& f, hipStream_t stream) {
-  // as many workgroups as stay resident (more would only take no item)
-  static int resident[2] = {0, 0};   // per-kernel cache: [0] per-CU blocks, [1] CUs
-  if (resident[0] == 0) {
-    int dev = 0, per_cu = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return -1;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_moe_fused<FMT, MS, NSTG, NSTD, PACKED>, 256, 0) !=
-        hipSuccess)
-      return -1;
-    resident[1] = cus;
-    resident[0] = per_cu > 0 ? per_cu : 1;
-  }
-  const dim3 grid(resident[0] * resident[1]);
-  hipLaunchKernelGGL((k_moe_fused<FMT, MS, NSTG, NSTD, PACKED>), grid, dim3(256), 0, stream, g, d, f);
+  // the largest item count: every work-list entry the bound allows
+  const long items = (long)g.max_tiles * (g.F / 32 + g.H / 64) + (long)f.T * ((g.H / 4 + 255) / 256);
+  hipLaunchKernelGGL((k_moe_fused<FMT, MS, NSTG, NSTD, PACKED>), dim3((unsigned)items), dim3(256), 0, stream, g, d,
+                     f);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -3,7 +3,7 @@
 // description, section 2; W4A4 / W8A8 per Miles docs section 5.3; the expert
 // layout of the NVFP4 / MXFP8 checkpoint, SGLang cookbook section 2
 // "Checkpoints").  Used by the per-GEMM kernels (gemm.hip) and by the
-// persistent expert-half kernel (fused.hip).
+// single-launch expert-half kernel (fused.hip).
 //
 // Work: the dispatch work list holds one entry per (local expert, block of
 // TM = 16*MS sorted rows); one tile is one entry x one 64-row slice of the

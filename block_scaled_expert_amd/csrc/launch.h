@@ -101,7 +101,7 @@ int launch_gemm_big(const GemmArgs& a, int stage, hipStream_t stream);
 int launch_gemm_gateup(const GemmArgs& a, hipStream_t stream);
 int launch_gemm_down(const GemmArgs& a, hipStream_t stream);
 
-// The expert half as one persistent launch (fused.hip) for work-list entries
+// The expert half as one launch (fused.hip) for work-list entries
 // of 16 to 64 rows.  ctl: fused_ctl_words(max_tiles) int32 words, zero when
 // the launch starts (the quantize + dispatch launch before it clears them).
 struct FusedArgs {

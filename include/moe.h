@@ -274,21 +274,21 @@ int moe_forward(const moe_config* cfg, const void* x, int32_t T, const int32_t* 
                 const float* topk_w, const moe_expert_weights* weights, void* out,
                 void* ws, size_t ws_bytes, void* stream, void* const* events);
 
-/* moe_forward as a persistent launch: the single-launch fused MoE of the
- * pages (SGLang blog "SGLang and Miles Add Day-0 Support for Inkling 2
- * Small", "Performance"; SGLang cookbook "Inkling-2-Small" section 2,
- * "MegaMoE").  After the one-launch x quantization + dispatch, one kernel
- * runs gate/up + capped SwiGLU, h quantization, down and the combine as
- * work items taken from a device-side queue; an item waits only on items
- * before it in the queue, so the queue drains whatever the number of
- * resident workgroups.  Each wait is also bounded (about a second of
+/* moe_forward with the expert half in one launch: the single-launch fused
+ * MoE of the pages (SGLang blog "SGLang and Miles Add Day-0 Support for
+ * Inkling 2 Small", "Performance"; SGLang cookbook "Inkling-2-Small"
+ * section 2, "MegaMoE").  After the one-launch x quantization + dispatch,
+ * one kernel runs gate/up + capped SwiGLU, h quantization, down and the
+ * combine as work items, one workgroup each, in the order a device-side
+ * counter hands them out; an item waits only on items before it, so the
+ * launch drains whatever the number of resident workgroups.  Each wait is also bounded (about a second of
  * polling; reaching the bound needs a device fault elsewhere): a wait that
  * runs out sets an error word in the workspace, every later wait returns at
  * once, the launch completes and `out` is undefined.  Same arguments, workspace,
  * result (bit-identical to moe_forward) and errors as moe_forward.  It
  * applies when T * top_k <= 4096 and the expected rows per local expert
  * (T * top_k / num_experts) are at most 48; other batches run moe_forward's
- * launch sequence.  events: the GATE_UP pair times the persistent launch;
+ * launch sequence.  events: the GATE_UP pair times the single launch;
  * the QUANT_H, DOWN and COMBINE pairs are recorded back to back after it. */
 int moe_forward_fused(const moe_config* cfg, const void* x, int32_t T, const int32_t* topk_ids,
                       const float* topk_w, const moe_expert_weights* weights, void* out,

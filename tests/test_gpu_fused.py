@@ -1,10 +1,10 @@
-"""moe_forward_fused (the persistent single-launch expert half) on the GPU.
+"""moe_forward_fused (the expert half in one launch) on the GPU.
 
 Its work items run the same tile bodies, the same h quantization and the
 same fixed-order combine as moe_forward's launch sequence, so the two
 outputs must be bit-identical; each is also held to the oracle's bar
 (max|gpu - oracle| / max|oracle| <= 2e-2, routing replayed).  Shapes cover
-all three work-list entry heights the persistent launch serves (16, 32 and
+all three work-list entry heights the single launch serves (16, 32 and
 64 rows), both formats and weight layouts, EP shares (partial sums), a
 single token, Inkling-size decode batches, repeated calls on one workspace
 (the control words are cleared by each call's dispatch launch) and a batch
@@ -36,7 +36,7 @@ CASES = {
     # skewed loads: many experts with one entry, a few with several
     "zipf_nvfp4": synth.Workload("zipf_nvfp4", "skewed", 96, 512, 64, 6, 256, "nvfp4", 43, bias="zipf",
                                  weights="gaussian"),
-    # 128-row entries: outside the persistent launch's range
+    # 128-row entries: outside the single launch's range
     "many_rows": SMALL["many_rows"],
 }
 
@@ -104,7 +104,7 @@ def test_fused_repeated_calls_one_workspace(gpu_lib):
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
 def test_fused_cap_forms_under_stress(gpu_lib, form, fmt):
     """Expert weights x10 so gate/up values pass the cap: every capped-SwiGLU
-    form in the persistent launch's gate/up items."""
+    form in the single launch's gate/up items."""
     w = synth.Workload("cap", "cap stress", 48, 512, 16, 4, 256, fmt, 27, weights="gaussian")
     a = run_layer(gpu_lib, w, gain=10.0, cap_form=form)
     b = run_layer(gpu_lib, w, gain=10.0, cap_form=form, fused=True)

@@ -7,7 +7,7 @@ Each replay, separated by unrelated eager work and synchronizations, must
 reproduce the eager result bit for bit (same kernels, same fixed orders).
 Shapes cover the small-batch fused quantize + dispatch launch, the general
 dispatch, both GEMM kernels (decode tiles and 128-row tiles) in both
-formats, and the persistent single-launch expert half.
+formats, and the single-launch expert half.
 """
 import numpy as np
 import pytest
@@ -23,12 +23,12 @@ SHAPES = {
     "big_tiles_mxfp8": synth.Workload("g2", "graph", 700, 256, 8, 2, 128, "mxfp8", 32, weights="gaussian"),
     "big_tiles_nvfp4_general_dispatch": synth.Workload("g3", "graph", 600, 256, 16, 8, 128, "nvfp4", 33,
                                                        weights="gaussian"),
-    # the persistent launch (moe_forward_fused): its control words are cleared
+    # the single-launch expert half (moe_forward_fused): its control words are cleared
     # by the quantize + dispatch kernel of the same step, not by a memset
-    "persistent_nvfp4": synth.Workload("g4", "graph", 100, 1024, 32, 4, 512, "nvfp4", 34, weights="gaussian"),
-    "persistent_mxfp8": synth.Workload("g5", "graph", 64, 512, 48, 8, 256, "mxfp8", 35, weights="gaussian"),
+    "single_launch_nvfp4": synth.Workload("g4", "graph", 100, 1024, 32, 4, 512, "nvfp4", 34, weights="gaussian"),
+    "single_launch_mxfp8": synth.Workload("g5", "graph", 64, 512, 48, 8, 256, "mxfp8", 35, weights="gaussian"),
 }
-FUSED = {"persistent_nvfp4", "persistent_mxfp8"}
+FUSED = {"single_launch_nvfp4", "single_launch_mxfp8"}
 
 
 @pytest.mark.parametrize("key", list(SHAPES))
