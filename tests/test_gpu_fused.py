@@ -7,8 +7,9 @@ outputs must be bit-identical; each is also held to the oracle's bar
 all three work-list entry heights the single launch serves (16, 32 and
 64 rows), both formats and weight layouts, EP shares (partial sums), a
 single token, Inkling-size decode batches, repeated calls on one workspace
-(the control words are cleared by each call's dispatch launch) and a batch
-outside its range (128-row entries: moe_forward's launch sequence runs).
+(the control words are cleared by each call's dispatch launch) and batches
+outside its range (128-row entries, more than 4096 pairs: moe_forward's
+launch sequence runs).
 """
 import numpy as np
 import pytest
@@ -38,6 +39,10 @@ CASES = {
                                  weights="gaussian"),
     # 128-row entries: outside the single launch's range
     "many_rows": SMALL["many_rows"],
+    # more than 4096 pairs with 64-row entries: outside its range too (the
+    # general dispatch runs, then moe_forward's launch sequence)
+    "pairs_over_4096": synth.Workload("pairs_over_4096", "general dispatch", 600, 256, 128, 8, 128, "nvfp4", 44,
+                                      weights="gaussian"),
 }
 
 
