@@ -30,9 +30,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("moe_route", "moe_quantize_act", "moe_forward", "moe_dispatch", "moe_prepare_weights",
-              "moe_workspace_size", "moe_status_string", "moe_check_arch", "moe_validate_config",
-              "moe_encode_weights", "moe_decode_weights"):
+    for n in ("moe_route", "moe_quantize_act", "moe_forward", "moe_forward_fused", "moe_dispatch",
+              "moe_prepare_weights", "moe_workspace_size", "moe_status_string", "moe_check_arch",
+              "moe_validate_config", "moe_encode_weights", "moe_decode_weights"):
         assert n in names
 
 
@@ -111,6 +111,14 @@ def test_host_checks_before_device(lib):
     # zero tokens is a no-op that needs no device
     assert lib.moe_forward(ctypes.byref(cc), None, 0, None, None, None, None, ctypes.c_void_p(0x1000), n.value,
                            None, None) == 0
+    # the single-launch variant checks its arguments the same way
+    assert lib.moe_forward_fused(ctypes.byref(cc), None, 65, None, None, None, None, None, 0, None, None) == -4
+    assert lib.moe_forward_fused(ctypes.byref(cc), None, 8, None, None, None, None, ctypes.c_void_p(0x1001),
+                                 n.value, None, None) == -1
+    assert lib.moe_forward_fused(ctypes.byref(cc), None, 8, None, None, None, None, ctypes.c_void_p(0x1000),
+                                 n.value - 1, None, None) == -3
+    assert lib.moe_forward_fused(ctypes.byref(cc), None, 0, None, None, None, None, ctypes.c_void_p(0x1000),
+                                 n.value, None, None) == 0
     # bad quantize arguments
     assert lib.moe_quantize_act(1, 0, None, 4, 48, None, None, None, None) == -1   # cols % 32
     assert lib.moe_quantize_act(3, 0, None, 4, 64, None, None, None, None) == -5   # format
