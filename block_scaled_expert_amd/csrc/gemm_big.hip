@@ -424,6 +424,10 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
     auto pack = [](const v2h (&x)[4]) {
       return v8h{x[0][0], x[0][1], x[1][0], x[1][1], x[2][0], x[2][1], x[3][0], x[3][1]};
     };
+    // gate/up: a wave in its k step issues ahead of the waves in the step
+    // barrier, loads or epilogue (prefill gate/up 4.79 -> 4.68 ms on one
+    // box; the down kernel did not gain)
+    if constexpr (STAGE == 0) __builtin_amdgcn_s_setprio(1);
     v2h bx[2][2][4];   // [part parity][column group][pair]
     v2h sx[4];
 #pragma unroll
@@ -460,6 +464,7 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (STAGE == 0) __builtin_amdgcn_s_setprio(0);
   };
 
   // main loop: PF steps of weights and activations in flight (as in
