@@ -292,7 +292,11 @@ __device__ __forceinline__ void expert_tile(const GemmArgs& a, int tile, int bx,
     for (int j = 0; j < PF && j < NST; j++) issue(s0 + j, fa[j], fb[j]);
 #pragma unroll
     for (int s = 0; s < NST; s++) {
+      // a wave whose operands have arrived issues ahead of the others
+      // (MXFP8 decode gate/up 557 -> 544 us on one box)
+      __builtin_amdgcn_s_setprio(1);
       step_compute<FMT, MS, NCG>(fa[s % PF], fb[s % PF], acc);
+      __builtin_amdgcn_s_setprio(0);
       if (s + PF < NST) issue(s0 + s + PF, fa[s % PF], fb[s % PF]);
     }
   } else {
