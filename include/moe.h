@@ -152,8 +152,11 @@ int moe_check_arch(const char* arch);
  * MOE_ERR_UNSUPPORTED_FORMAT. */
 int moe_validate_config(const moe_config* cfg);
 
-/* Bytes of workspace moe_route, moe_dispatch and moe_forward need for up to
- * cfg->max_tokens tokens.  Host only; *bytes is a host pointer. */
+/* Bytes of workspace moe_route, moe_dispatch, moe_forward and
+ * moe_forward_fused need for up to cfg->max_tokens tokens.  Host only;
+ * *bytes is a host pointer.  The workspace needs no initial contents: every
+ * call writes what it later reads (moe_forward_fused's control words are
+ * cleared by its own first launch). */
 int moe_workspace_size(const moe_config* cfg, size_t* bytes);
 
 /* Per-row activation quantization (the W4A4 / W8A8 step; Miles docs section
