@@ -42,10 +42,10 @@ pages print no worked numeric example of the layer.
 from .formats import (  # noqa: F401
     E2M1_MAG, E4M3_MAG, e2m1_encode, e2m1_decode, e4m3_encode, e4m3_decode,
     e8m0_decode, bf16_round_f64, bf16_bits_to_f32,
-    quantize_mxfp8, dequantize_mxfp8, quantize_nvfp4, dequantize_nvfp4,
+    quantize_mxfp8, dequantize_mxfp8, quantize_nvfp4, dequantize_nvfp4, nvfp4_global_scale,
     pack_nibbles, unpack_nibbles,
 )
 from .layer import (  # noqa: F401
-    OracleConfig, route, dispatch, expert_forward, moe_layer,
+    OracleConfig, route, dispatch, expert_forward, expert_gate_up, expert_down, moe_layer, combine, act_scale,
     quantize_expert_weights, dequantize_expert, cap_swiglu,
 )

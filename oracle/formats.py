@@ -21,7 +21,9 @@ Readings where the pages are silent (each also stated in the design doc):
   degenerate NVFP4 block whose scale product underflows) encodes as +0.
 * R1/R2 (NVFP4 fp32 scale): per row of an activation matrix (the scale must
   cover the expert's whole input width, SGLang cookbook section 2
-  "Parallelism"), per whole (expert, matrix) tensor for weights.
+  "Parallelism"), per whole (expert, matrix) tensor for weights.  Two
+  alternatives for activations are kept selectable: one scale for the whole
+  activation tensor of a call ("tensor"), or a fixed scale ("static").
   gs = amax / 2688 (2688 = 6 * 448); block scale s = E4M3(a_b / (6*gs));
   reciprocal r = 1 / (s*gs); codes E2M1(v * r).  Every step is one IEEE fp32
   operation (division, then multiplication), never fused.
@@ -212,31 +214,51 @@ def _nvfp4_blocks(blocks: np.ndarray, gs: np.ndarray):
     return codes, sc
 
 
-def quantize_nvfp4(v: np.ndarray, domain: str = "row"):
+def nvfp4_global_scale(amax) -> np.ndarray:
+    """fp32 scale of an NVFP4 scale domain with maximum magnitude amax:
+    amax / 2688 as one IEEE fp32 division (2688 = 6 * 448, the largest E2M1
+    value times the largest E4M3 value), and 1.0 for an all-zero domain."""
+    A = np.asarray(amax, dtype=_F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(A == 0, _F32(1.0), (A / _F32(2688.0)).astype(_F32)).astype(_F32)
+
+
+def quantize_nvfp4(v: np.ndarray, domain: str = "row", gs=None):
     """Quantize fp32 rows [R, K] (K % 16 == 0) to NVFP4.
 
     domain="row": one fp32 scale per row (activations, reading R1).
-    domain="tensor": one fp32 scale for the whole array (weights, R2).
+    domain="tensor": one fp32 scale for the whole array (weights, R2; the
+        per-tensor alternative of R1 for activations).
+    domain="static": the given fp32 scale `gs` for every row (the static
+        alternative of R1: a scale fixed ahead of time, not taken from the
+        data; block scales and codes saturate where the data exceed it).
 
-    Returns (packed codes uint8 [R, K/2], scales uint8 [R, K/16], gs fp32
-    [R] for "row" or a 0-d fp32 array for "tensor").
+    Row and tensor domains whose maximum is 0 take gs = 1 and all-zero codes
+    and scales.  Returns (packed codes uint8 [R, K/2], scales uint8 [R, K/16],
+    gs fp32 [R] for "row" or a 0-d fp32 array for "tensor" / "static").
     """
     v = np.asarray(v, dtype=np.float32)
     assert v.ndim == 2 and v.shape[1] % NV_BLOCK == 0
     R, K = v.shape
     if domain == "row":
-        A = np.max(np.abs(v), axis=1)                               # fp32 [R]
+        A = np.max(np.abs(v), axis=1).astype(_F32)                  # fp32 [R]
     elif domain == "tensor":
-        A = np.max(np.abs(v)).reshape(())                           # fp32 []
+        A = np.max(np.abs(v)).reshape(()).astype(_F32) if v.size else np.zeros((), _F32)
+    elif domain == "static":
+        if gs is None or not (np.float32(gs) > 0 and np.isfinite(np.float32(gs))):
+            raise ValueError("a static NVFP4 scale must be a positive finite fp32 value")
+        A = None
     else:
         raise ValueError(domain)
-    A = A.astype(_F32)
-    with np.errstate(divide="ignore", invalid="ignore"):
-        gs = np.where(A == 0, _F32(1.0), (A / _F32(2688.0)).astype(_F32)).astype(_F32)
+    if A is not None:
+        gs = nvfp4_global_scale(A)
+        zero = np.broadcast_to(A == 0, (R,))
+    else:
+        gs = np.asarray(gs, dtype=_F32).reshape(())
+        zero = np.zeros(R, dtype=bool)
     blocks = v.reshape(R, K // NV_BLOCK, NV_BLOCK)
-    gs_rows = np.broadcast_to(gs, (R,)) if domain == "tensor" else gs
+    gs_rows = np.broadcast_to(gs, (R,)) if gs.ndim == 0 else gs
     codes, sc = _nvfp4_blocks(blocks, gs_rows)
-    zero = np.broadcast_to(A == 0, (R,))
     codes = np.where(zero[:, None, None], np.uint8(0), codes)
     sc = np.where(zero[:, None], np.uint8(0), sc).astype(np.uint8)
     return pack_nibbles(codes.reshape(R, K)), sc, gs

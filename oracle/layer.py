@@ -36,6 +36,12 @@ Readings taken where the pages are silent (numbered as in the design doc):
 * R12 expert-parallel share: only experts in [expert_begin,
       expert_begin + num_local) are computed; gate weights keep their
       normalisation over all k; out is the partial sum over local experts.
+* R1  NVFP4 activation fp32 scale (act_gs): "row" (default) -- one scale per
+      row over its full width, x rows for gate/up and (token, expert) h rows
+      for down; "tensor" -- one scale over the whole activation tensor of the
+      call (all T x rows; all local (token, expert) h rows); "static" -- the
+      fixed scales act_gs_static = (x scale, h scale).  MXFP8 has no fp32
+      scale and ignores act_gs.
 """
 from __future__ import annotations
 
@@ -66,6 +72,8 @@ class OracleConfig:
     cap: float = 7.0
     norm_topk: bool = True
     routed_scale: float = 1.0
+    act_gs: str = "row"                       # "row" | "tensor" | "static" (NVFP4 only)
+    act_gs_static: tuple = (1.0, 1.0)         # (x scale, h scale) when act_gs == "static"
 
     @property
     def local(self) -> range:
@@ -151,15 +159,36 @@ def dispatch(cfg: OracleConfig, topk_ids: np.ndarray):
 # Quantization of activations (step 4) and of weights
 # --------------------------------------------------------------------------
 
-def quantize_rows(fmt: str, v: np.ndarray):
-    """Per-row activation quantization of fp32 rows; returns a dict."""
+def quantize_rows(fmt: str, v: np.ndarray, gs=None):
+    """Activation quantization of fp32 rows; returns a dict.  NVFP4: with
+    gs None each row takes its own fp32 scale (reading R1); otherwise every
+    row takes the given fp32 scale (the per-tensor and static alternatives)."""
     if fmt == "mxfp8":
         c, s = F.quantize_mxfp8(v)
         return dict(codes=c, scales=s)
     if fmt == "nvfp4":
-        c, s, g = F.quantize_nvfp4(v, domain="row")
+        if gs is None:
+            c, s, g = F.quantize_nvfp4(v, domain="row")
+        else:
+            c, s, g = F.quantize_nvfp4(v, domain="static", gs=gs)
         return dict(codes=c, scales=s, gs=g)
     raise ValueError(fmt)
+
+
+def act_scale(cfg: OracleConfig, site: int, v_all: np.ndarray):
+    """The fp32 scale every row of an activation tensor shares under act_gs
+    "tensor" (from the maximum over v_all, the whole tensor of the call) or
+    "static" (act_gs_static[site]; site 0 = x, 1 = h); None for "row" and for
+    MXFP8."""
+    if cfg.fmt != "nvfp4" or cfg.act_gs == "row":
+        return None
+    if cfg.act_gs == "static":
+        return np.float32(cfg.act_gs_static[site])
+    if cfg.act_gs == "tensor":
+        v_all = np.asarray(v_all, dtype=np.float32)
+        A = np.max(np.abs(v_all)) if v_all.size else np.float32(0.0)
+        return F.nvfp4_global_scale(A)[()]
+    raise ValueError(cfg.act_gs)
 
 
 def dequantize_rows(fmt: str, q: dict) -> np.ndarray:
@@ -222,16 +251,27 @@ def cap_swiglu(cfg: OracleConfig, g32: np.ndarray, u32: np.ndarray) -> np.ndarra
     return h.astype(np.float32)
 
 
-def expert_forward(cfg: OracleConfig, xq64: np.ndarray, wdeq):
-    """One expert on rows of dequantized activations (float64 [n, H]).
-    Returns fp32 y [n, H] and the intermediate fp32 h [n, F]."""
-    gate, up, down = wdeq
+def expert_gate_up(cfg: OracleConfig, xq64: np.ndarray, wdeq) -> np.ndarray:
+    """Gate/up projection and capped SwiGLU of one expert on rows of
+    dequantized activations (float64 [n, H]); fp32 h [n, F]."""
+    gate, up, _ = wdeq
     g = (xq64 @ gate.T).astype(np.float32)
     u = (xq64 @ up.T).astype(np.float32)
-    h = cap_swiglu(cfg, g, u)
-    hq = dequantize_rows(cfg.fmt, quantize_rows(cfg.fmt, h))
-    y = (hq @ down.T).astype(np.float32)
-    return y, h
+    return cap_swiglu(cfg, g, u)
+
+
+def expert_down(cfg: OracleConfig, h: np.ndarray, wdeq, h_gs=None) -> np.ndarray:
+    """h quantized per row (or with the shared scale h_gs, see act_scale),
+    then the down projection; fp32 y [n, H]."""
+    hq = dequantize_rows(cfg.fmt, quantize_rows(cfg.fmt, h, gs=h_gs))
+    return (hq @ wdeq[2].T).astype(np.float32)
+
+
+def expert_forward(cfg: OracleConfig, xq64: np.ndarray, wdeq, h_gs=None):
+    """One expert on rows of dequantized activations (float64 [n, H]).
+    Returns fp32 y [n, H] and the intermediate fp32 h [n, F]."""
+    h = expert_gate_up(cfg, xq64, wdeq)
+    return expert_down(cfg, h, wdeq, h_gs), h
 
 
 # --------------------------------------------------------------------------
@@ -247,33 +287,62 @@ def moe_layer(cfg: OracleConfig, x_bf16, w_router_bf16, bias, expert_weights,
     tokens: optional array of token indices; only those outputs are computed
     (the router still runs on those tokens only).
     topk_ids/topk_w: optional routing replay (replaces the router's choice).
+    Under act_gs "tensor" the x scale is taken over all T tokens even when
+    `tokens` selects some; the h scale needs every local pair's h, so
+    `tokens` must then be None.
     Returns dict(out=bf16 bits uint16 [n, H], route=..., y=..., tokens=...).
     """
     x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
     T = x_bf16.shape[0]
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    per_tensor = cfg.fmt == "nvfp4" and cfg.act_gs == "tensor"
+    if per_tensor and tokens is not None:
+        raise ValueError("act_gs 'tensor': the h scale spans every token; pass tokens=None")
     xs = x_bf16[tok]
     r = route(cfg, xs, w_router_bf16, bias)
     ids = r["topk_ids"] if topk_ids is None else np.asarray(topk_ids, dtype=np.int32)[tok]
     tw = r["topk_w"] if topk_w is None else np.asarray(topk_w, dtype=np.float32)[tok]
 
-    xq = dequantize_rows(cfg.fmt, quantize_rows(cfg.fmt, F.bf16_bits_to_f32(xs)))
+    x_gs = act_scale(cfg, 0, F.bf16_bits_to_f32(x_bf16))
+    xq = dequantize_rows(cfg.fmt, quantize_rows(cfg.fmt, F.bf16_bits_to_f32(xs), gs=x_gs))
     n, k = ids.shape
     H = cfg.hidden
     y = np.zeros((n, k, H), dtype=np.float32)
     have = np.zeros((n, k), dtype=bool)
     get = expert_weights if callable(expert_weights) else (lambda e: expert_weights[e - cfg.expert_begin])
-    for e in cfg.local:                                   # expert-index order
-        rows, slots = np.nonzero(ids == e)
-        if rows.size == 0:
-            continue
-        wdeq = dequantize_expert(cfg.fmt, get(e))
-        ye, _ = expert_forward(cfg, xq[rows], wdeq)
-        y[rows, slots] = ye
-        have[rows, slots] = True
+    if not per_tensor:
+        h_gs = act_scale(cfg, 1, None) if cfg.act_gs == "static" else None
+        for e in cfg.local:                               # expert-index order
+            rows, slots = np.nonzero(ids == e)
+            if rows.size == 0:
+                continue
+            wdeq = dequantize_expert(cfg.fmt, get(e))
+            ye, _ = expert_forward(cfg, xq[rows], wdeq, h_gs)
+            y[rows, slots] = ye
+            have[rows, slots] = True
+    else:
+        # every local pair's h first: its shared scale spans all of them
+        hs = {}
+        for e in cfg.local:
+            rows, slots = np.nonzero(ids == e)
+            if rows.size:
+                hs[e] = (rows, slots, expert_gate_up(cfg, xq[rows], dequantize_expert(cfg.fmt, get(e))))
+        h_all = np.concatenate([v[2] for v in hs.values()]) if hs else np.zeros((0, cfg.ffn), np.float32)
+        h_gs = act_scale(cfg, 1, h_all)
+        for e, (rows, slots, h) in hs.items():
+            y[rows, slots] = expert_down(cfg, h, dequantize_expert(cfg.fmt, get(e)), h_gs)
+            have[rows, slots] = True
 
-    acc = np.zeros((n, H), dtype=np.float64)
+    out = combine(tw, y, have)
+    return dict(out=out, route=r, topk_ids=ids, topk_w=tw, y=y, have=have, tokens=tok, x_gs=x_gs)
+
+
+def combine(tw: np.ndarray, y: np.ndarray, have: np.ndarray) -> np.ndarray:
+    """Weighted combine: out[t] = bf16_rne(sum_j tw[t, j] * y[t, j]) over the
+    pairs that were computed (have), summed in float64 in fixed j order.
+    tw fp32 [n, k]; y fp32 [n, k, H]; have bool [n, k].  Returns bf16 bits."""
+    n, k = have.shape
+    acc = np.zeros((n, y.shape[2]), dtype=np.float64)
     for j in range(k):                                    # fixed j order
         acc = acc + np.where(have[:, j:j + 1], tw[:, j:j + 1].astype(np.float64) * y[:, j].astype(np.float64), 0.0)
-    out = F.bf16_round_f64(acc)
-    return dict(out=out, route=r, topk_ids=ids, topk_w=tw, y=y, have=have, tokens=tok)
+    return F.bf16_round_f64(acc)
