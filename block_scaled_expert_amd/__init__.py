@@ -3,8 +3,9 @@
 Argument marshalling only: every step of the layer runs in the library's HIP
 kernels on the caller's current torch stream.  The functions mirror the C
 ABI in include/moe.h (moe_route, moe_dispatch, moe_quantize_act,
-moe_forward, moe_forward_fused, moe_workspace_size, moe_check_arch,
-moe_status_string).
+moe_forward, moe_forward_fused, moe_forward_fused_status, moe_cap_swiglu,
+moe_workspace_size, moe_check_arch, moe_status_string, the weight encoder
+and decoder).
 Tensors must be contiguous and on the current CUDA (HIP) device; the library
 never allocates, so callers pass outputs and a workspace.
 
@@ -23,11 +24,14 @@ FMT_NVFP4, FMT_MXFP8 = 1, 2
 FMTS = {"nvfp4": FMT_NVFP4, "mxfp8": FMT_MXFP8}
 CAP_SOFT_GATE_UP, CAP_HARD_GATE_UP, CAP_SOFT_OUT, CAP_NONE = 0, 1, 2, 3
 DTYPE_BF16, DTYPE_F32 = 0, 1
+ACT_GS_PER_ROW, ACT_GS_PER_TENSOR, ACT_GS_STATIC = 0, 1, 2
+ACT_GS_SCRATCH_BYTES = 1028   # moe_quantize_act's scratch for a per-tensor NVFP4 scale
 STAGES = ("quant_x", "dispatch", "gate_up", "quant_h", "down", "combine")
 
 EXPORTED = ("moe_status_string", "moe_check_arch", "moe_validate_config", "moe_workspace_size",
             "moe_quantize_act", "moe_route", "moe_dispatch", "moe_prepare_weights", "moe_forward",
-            "moe_forward_fused", "moe_encode_weights", "moe_decode_weights")
+            "moe_forward_fused", "moe_forward_fused_status", "moe_cap_swiglu", "moe_encode_weights",
+            "moe_decode_weights")
 LAYOUT_CANONICAL, LAYOUT_PACKED = 0, 1
 
 
@@ -42,7 +46,7 @@ class CConfig(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("expert_begin", ctypes.c_int32),
                 ("num_local_experts", ctypes.c_int32), ("fmt", ctypes.c_int32), ("cap_form", ctypes.c_int32),
                 ("cap", ctypes.c_float), ("norm_topk", ctypes.c_int32), ("routed_scale", ctypes.c_float),
-                ("max_tokens", ctypes.c_int32)]
+                ("max_tokens", ctypes.c_int32), ("act_gs", ctypes.c_int32), ("act_gs_static", ctypes.c_float * 2)]
 
 
 class CWeights(ctypes.Structure):
@@ -67,7 +71,9 @@ def load() -> ctypes.CDLL:
     lib.moe_check_arch.argtypes = [ctypes.c_char_p]
     lib.moe_validate_config.argtypes = [ctypes.POINTER(CConfig)]
     lib.moe_workspace_size.argtypes = [ctypes.POINTER(CConfig), ctypes.POINTER(sz)]
-    lib.moe_quantize_act.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp]
+    lib.moe_quantize_act.argtypes = [ctypes.POINTER(CConfig), i32, i32, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_cap_swiglu.argtypes = [ctypes.POINTER(CConfig), vp, vp, ctypes.c_int64, vp, vp]
+    lib.moe_forward_fused_status.argtypes = [ctypes.POINTER(CConfig), i32, vp, sz, vp, vp]
     lib.moe_encode_weights.argtypes = [i32, i32, vp, i32, i32, i32, vp, vp, vp, i32, i32, vp, sz, vp]
     lib.moe_decode_weights.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
     lib.moe_route.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -106,6 +112,8 @@ class Config:
     norm_topk: bool = True
     routed_scale: float = 1.0
     max_tokens: int = 64
+    act_gs: int = ACT_GS_PER_ROW
+    act_gs_static: tuple = (1.0, 1.0)
 
     @property
     def num_local(self) -> int:
@@ -116,7 +124,7 @@ class Config:
             raise ValueError(f"unknown format {self.fmt!r}")
         return CConfig(self.hidden, self.ffn, self.num_experts, self.top_k, self.expert_begin, self.num_local,
                        FMTS[self.fmt], self.cap_form, self.cap, int(bool(self.norm_topk)), self.routed_scale,
-                       self.max_tokens)
+                       self.max_tokens, self.act_gs, (ctypes.c_float * 2)(*self.act_gs_static))
 
 
 def _ok(status: int, what: str) -> None:
@@ -155,20 +163,48 @@ def workspace(cfg: Config, device="cuda"):
     return torch.empty(workspace_size(cfg), dtype=torch.uint8, device=device)
 
 
-def quantize_act(fmt: str, x, codes, scales, row_gs=None) -> None:
-    """Per-row NVFP4 / MXFP8 quantization of a bf16 or fp32 [rows, cols] tensor."""
+def quantize_act(cfg, x, codes, scales, row_gs=None, site: int = 0, ws=None) -> None:
+    """NVFP4 / MXFP8 quantization of a bf16 or fp32 [rows, cols] tensor in
+    cfg's format and activation-scale mode (cfg: a Config, or a format name
+    for the per-row default).  site 0: gate/up input x, 1: down input h.
+    ws: uint8 scratch of at least ACT_GS_SCRATCH_BYTES for NVFP4 per-tensor
+    scales."""
     import torch
+    if isinstance(cfg, str):
+        cfg = Config(fmt=cfg)
     rows, cols = x.shape
     dt = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32}.get(x.dtype)
     if dt is None:
         raise ValueError("x must be bfloat16 or float32")
-    nv = fmt == "nvfp4"
+    nv = cfg.fmt == "nvfp4"
     _ptr(x, name="x")
-    args = (FMTS[fmt], dt, _ptr(x), rows, cols,
+    cc = cfg.c()
+    args = (ctypes.byref(cc), site, dt, _ptr(x), rows, cols,
             _ptr(codes, torch.uint8, (rows, cols // 2 if nv else cols), "codes"),
             _ptr(scales, torch.uint8, (rows, cols // (16 if nv else 32)), "scales"),
-            _ptr(row_gs, torch.float32, (rows,), "row_gs") if nv else None, _stream())
+            _ptr(row_gs, torch.float32, (rows,), "row_gs") if nv else None,
+            _ptr(ws, torch.uint8, None, "ws"), 0 if ws is None else ws.numel(), _stream())
     _ok(load().moe_quantize_act(*args), "moe_quantize_act")
+
+
+def cap_swiglu(cfg: Config, g, u, h) -> None:
+    """The expert epilogue's capped SwiGLU on fp32 tensors of equal size."""
+    import torch
+    n = g.numel()
+    cc = cfg.c()
+    _ok(load().moe_cap_swiglu(ctypes.byref(cc), _ptr(g, torch.float32, None, "g"),
+                              _ptr(u, torch.float32, (n,) if u.dim() == 1 else None, "u"), n,
+                              _ptr(h, torch.float32, None, "h"), _stream()), "moe_cap_swiglu")
+
+
+def forward_fused_status(cfg: Config, T: int, ws, err) -> None:
+    """err (int32 device tensor of one element) <- the error word of the last
+    moe_forward_fused call on ws for T tokens (0: every wait was met)."""
+    import torch
+    cc = cfg.c()
+    _ok(load().moe_forward_fused_status(ctypes.byref(cc), T, _ptr(ws, torch.uint8, None, "ws"), ws.numel(),
+                                        _ptr(err, torch.int32, (1,), "err"), _stream()),
+        "moe_forward_fused_status")
 
 
 def _check_gs(gs, nmat: int, group: int, stride: int) -> None:

@@ -2,6 +2,7 @@
 // check, workspace carving and the launch sequence.  Nothing here allocates,
 // frees or synchronizes; every launch goes on the caller's stream.
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/moe.h"
@@ -33,7 +34,7 @@ int n_local(const moe_config* c) { return c->num_local_experts; }
 
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct Layout {
-  size_t z, xq, xs, xg, counts, offsets, sorted, pos, work, ntiles, ctl, h, hq, hs, hg, y, total;
+  size_t z, xq, xs, xg, ags, counts, offsets, sorted, pos, work, ntiles, ctl, h, hq, hs, hg, y, total;
   int max_tiles, nchunks;
 };
 
@@ -54,6 +55,7 @@ Layout layout(const moe_config* c, int T) {
   L.xq = take((size_t)T * (nv ? H / 2 : H));
   L.xs = take((size_t)T * (nv ? H / 16 : H / 32));
   L.xg = take((size_t)T * 4);
+  L.ags = take(nv ? kActGsScratchBytes : 0);   // NVFP4 per-tensor scale: partial maxima + the scale
   // dispatch never uses more than 1024 chunks (see dispatch_chunk)
   L.counts = take((size_t)(1024 + 1) * EL * 4);
   L.offsets = take((EL + 1) * 4);
@@ -86,6 +88,45 @@ int check_ws(const moe_config* c, int T, void* ws, size_t ws_bytes) {
 
 void record(void* const* ev, int idx, hipStream_t s) {
   if (ev != nullptr && ev[idx] != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(ev[idx]), s);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Rows per work-list entry of a forward of T tokens.
+int forward_tile_m(const moe_config* c, int T) {
+  int tile_m = gemm_tile_m(T, c->top_k, c->num_experts);
+  if (tile_m == 128 && !gemm_big_supported(c->hidden, c->ffn)) tile_m = 64;
+  return tile_m;
+}
+
+// Whether moe_forward_fused runs its single expert-half launch for T tokens:
+// at most 4096 pairs (the one-launch quantize + dispatch), entries of at most
+// 64 rows, and NVFP4 activation scales per row (a per-tensor h scale needs
+// every h row before any is quantized).
+bool fused_applies(const moe_config* c, int T) {
+  const long P = (long)T * c->top_k;
+  const bool nv = c->fmt == MOE_FMT_NVFP4;
+  return T > 0 && P <= kSmallDispatchPairs && forward_tile_m(c, T) <= 64 &&
+         (!nv || c->act_gs == MOE_ACT_GS_PER_ROW);
+}
+
+// Where the NVFP4 activation rows of site 0 (x) / 1 (h) take their scale.
+ActGs act_gs_of(const moe_config* c, int site, float* scratch) {
+  ActGs a;
+  if (c->fmt != MOE_FMT_NVFP4) return a;
+  if (c->act_gs == MOE_ACT_GS_PER_TENSOR) {
+    a.mode = 1;
+    a.gs_dev = scratch;
+  } else if (c->act_gs == MOE_ACT_GS_STATIC) {
+    a.mode = 2;
+    a.gs_val = c->act_gs_static[site];
+  }
+  return a;
+}
+
+bool test_fail_requested() {
+  const char* v = std::getenv("MOE_FUSED_TEST_FAIL");
+  return v != nullptr && v[0] == '1';
 }
 
 }  // namespace
@@ -126,6 +167,10 @@ int moe_validate_config(const moe_config* c) {
   if (c->cap_form < MOE_CAP_SOFT_GATE_UP || c->cap_form > MOE_CAP_NONE) return MOE_ERR_INVALID_ARG;
   if (c->cap_form != MOE_CAP_NONE && !(c->cap > 0.0f)) return MOE_ERR_INVALID_ARG;
   if (c->max_tokens < 0 || (long)c->max_tokens * c->top_k > (1L << 26)) return MOE_ERR_INVALID_ARG;
+  if (c->act_gs < MOE_ACT_GS_PER_ROW || c->act_gs > MOE_ACT_GS_STATIC) return MOE_ERR_INVALID_ARG;
+  if (c->act_gs == MOE_ACT_GS_STATIC && c->fmt == MOE_FMT_NVFP4)
+    for (int i = 0; i < 2; i++)   // positive, finite, and 6 * 448 * gs stays finite
+      if (!(c->act_gs_static[i] > 0.0f && c->act_gs_static[i] <= 0x1p120f)) return MOE_ERR_INVALID_ARG;
   // the GEMM work list rides grid.y (at most 65535 entries)
   if (ceil_div((long)c->max_tokens * c->top_k, 16) + c->num_local_experts > 65535) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
@@ -139,21 +184,46 @@ int moe_workspace_size(const moe_config* c, size_t* bytes) {
   return MOE_OK;
 }
 
-int moe_quantize_act(int32_t fmt, int32_t dtype, const void* x, int32_t rows, int32_t cols,
-                     uint8_t* codes, uint8_t* scales, float* row_gs, void* stream) {
-  if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8) return MOE_ERR_UNSUPPORTED_FORMAT;
+int moe_quantize_act(const moe_config* c, int32_t site, int32_t dtype, const void* x, int32_t rows, int32_t cols,
+                     uint8_t* codes, uint8_t* scales, float* row_gs, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe_validate_config(c);
+  if (st != MOE_OK) return st;
+  const int fmt = c->fmt;
+  if (site != 0 && site != 1) return MOE_ERR_INVALID_ARG;
   if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
   if (rows < 0 || cols <= 0 || cols % 32 != 0) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
   if (x == nullptr || codes == nullptr || scales == nullptr) return MOE_ERR_INVALID_ARG;
-  if (fmt == MOE_FMT_NVFP4 && row_gs == nullptr) return MOE_ERR_INVALID_ARG;
-  const int d = device_check();
-  if (d != MOE_OK) return d;
-  return launch_quant(fmt, dtype, x, rows, nullptr, cols, codes, scales, row_gs,
-                      static_cast<hipStream_t>(stream)) == 0 ? MOE_OK : MOE_ERR_LAUNCH;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return MOE_ERR_INVALID_ARG;
+  const bool nv = fmt == MOE_FMT_NVFP4;
+  if (nv && (row_gs == nullptr || !aligned(row_gs, 4))) return MOE_ERR_INVALID_ARG;
+  const bool tensor = nv && c->act_gs == MOE_ACT_GS_PER_TENSOR;
+  if (tensor) {
+    if (ws == nullptr || !aligned(ws, 4)) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < kActGsScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
+  if ((st = device_check()) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int bad = 0;
+  if (tensor) bad |= launch_act_gs_tensor(dtype, x, rows, nullptr, cols, static_cast<float*>(ws), s);
+  bad |= launch_quant(fmt, dtype, x, rows, nullptr, cols, codes, scales, row_gs, s,
+                      act_gs_of(c, site, static_cast<float*>(ws)));
+  return bad ? MOE_ERR_LAUNCH : MOE_OK;
 }
 
-static bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+int moe_cap_swiglu(const moe_config* c, const float* g, const float* u, int64_t n, float* h, void* stream) {
+  int st = moe_validate_config(c);
+  if (st != MOE_OK) return st;
+  if (n < 0) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (g == nullptr || u == nullptr || h == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(g, 4) || !aligned(u, 4) || !aligned(h, 4)) return MOE_ERR_INVALID_ARG;
+  if ((st = device_check()) != MOE_OK) return st;
+  const float cap = c->cap_form == MOE_CAP_NONE ? 1.0f : c->cap;
+  return launch_cap_swiglu(c->cap_form, cap, g, u, (long)n, h, static_cast<hipStream_t>(stream)) == 0
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
 
 int moe_encode_weights(int32_t fmt, int32_t dtype, const void* w, int32_t nmat, int32_t rows, int32_t cols,
                        uint8_t* codes, uint8_t* scales, float* gs, int32_t gs_group, int32_t gs_stride,
@@ -205,6 +275,9 @@ int moe_route(const moe_config* c, const void* x, int32_t T, const void* w_route
   if (T == 0) return MOE_OK;
   if (x == nullptr || w_router == nullptr || bias == nullptr || topk_ids == nullptr || topk_w == nullptr)
     return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(bias, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4))
+    return MOE_ERR_INVALID_ARG;
   if ((st = device_check()) != MOE_OK) return st;
   const Layout L = layout(c, c->max_tokens);
   return launch_router(static_cast<const uint16_t*>(x), T, c->hidden, static_cast<const uint16_t*>(w_router),
@@ -220,6 +293,8 @@ int moe_dispatch(const moe_config* c, const int32_t* topk_ids, int32_t T, int32_
   if (st != MOE_OK) return st;
   if (T < 0 || expert_offsets == nullptr) return MOE_ERR_INVALID_ARG;
   if (T > 0 && topk_ids == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(topk_ids, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_pairs, 4) || !aligned(pair_pos, 4))
+    return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(c, T, ws, ws_bytes)) != MOE_OK) return st;
   if ((st = device_check()) != MOE_OK) return st;
   const Layout L = layout(c, c->max_tokens);
@@ -247,6 +322,9 @@ int moe_prepare_weights(const moe_config* c, const moe_expert_weights* src, moe_
     return MOE_ERR_INVALID_ARG;
   if (src->w13 == dst->w13 || src->w2 == dst->w2 || src->w13_sc == dst->w13_sc || src->w2_sc == dst->w2_sc)
     return MOE_ERR_INVALID_ARG;
+  for (const moe_expert_weights* w : {src, static_cast<const moe_expert_weights*>(dst)})
+    if (!aligned(w->w13, 16) || !aligned(w->w2, 16) || !aligned(w->w13_sc, 4) || !aligned(w->w2_sc, 4))
+      return MOE_ERR_INVALID_ARG;
   if ((st = device_check()) != MOE_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const long n = c->num_local_experts;
@@ -273,6 +351,11 @@ static int forward_impl(const moe_config* c, const void* x, int32_t T, const int
     return MOE_ERR_INVALID_ARG;
   if (c->fmt == MOE_FMT_NVFP4 && w->gs == nullptr) return MOE_ERR_INVALID_ARG;
   if (w->layout != MOE_LAYOUT_CANONICAL && w->layout != MOE_LAYOUT_PACKED) return MOE_ERR_INVALID_ARG;
+  // the kernels' 16-byte vector loads and stores
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w->w13, 16) || !aligned(w->w2, 16) ||
+      !aligned(w->w13_sc, 4) || !aligned(w->w2_sc, 4) || !aligned(w->gs, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4))
+    return MOE_ERR_INVALID_ARG;
   if ((st = device_check()) != MOE_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -282,8 +365,7 @@ static int forward_impl(const moe_config* c, const void* x, int32_t T, const int
   const bool nv = c->fmt == MOE_FMT_NVFP4;
   int bad = 0;
 
-  int tile_m = gemm_tile_m(T, k, c->num_experts);
-  if (tile_m == 128 && !gemm_big_supported(H, F)) tile_m = 64;
+  const int tile_m = forward_tile_m(c, T);
   DispatchBufs b{};
   b.counts = at<int32_t>(ws, L.counts);
   b.offsets = at<int32_t>(ws, L.offsets);
@@ -293,23 +375,28 @@ static int forward_impl(const moe_config* c, const void* x, int32_t T, const int
   b.ntiles = at<int32_t>(ws, L.ntiles);
   // the single launch covers work-list entries of 16 to 64 rows after
   // the one-launch quantize + dispatch (which also clears its control words)
-  fused = fused && P <= kSmallDispatchPairs && tile_m <= 64;
+  fused = fused && fused_applies(c, T);
+  float* const ags = at<float>(ws, L.ags);
+  const ActGs agx = act_gs_of(c, 0, ags), agh = act_gs_of(c, 1, ags);
   if (P <= kSmallDispatchPairs) {
     // 1 + 2. quantize x per row and dispatch (+ tile list) in one launch; the
     // quantize-x stage covers both, the dispatch stage is empty
     record(events, 2 * MOE_STAGE_QUANT_X, s);
+    if (agx.mode == 1) bad |= launch_act_gs_tensor(0, x, T, nullptr, H, ags, s);
     bad |= launch_prep_small(c->fmt, static_cast<const uint16_t*>(x), T, H, at<uint8_t>(ws, L.xq),
                              at<uint8_t>(ws, L.xs), at<float>(ws, L.xg), topk_ids, P, c->expert_begin, EL, tile_m,
                              b, fused ? at<int32_t>(ws, L.ctl) : nullptr,
-                             fused ? fused_ctl_words(L.max_tiles) : 0, s);
+                             fused ? fused_ctl_words(L.max_tiles) : 0, s, agx);
+    if (fused && test_fail_requested()) bad |= launch_fused_force_error(at<int32_t>(ws, L.ctl), s);
     record(events, 2 * MOE_STAGE_QUANT_X + 1, s);
     record(events, 2 * MOE_STAGE_DISPATCH, s);
     record(events, 2 * MOE_STAGE_DISPATCH + 1, s);
   } else {
     // 1. quantize x per row
     record(events, 2 * MOE_STAGE_QUANT_X, s);
+    if (agx.mode == 1) bad |= launch_act_gs_tensor(0, x, T, nullptr, H, ags, s);
     bad |= launch_quant(c->fmt, 0, x, T, nullptr, H, at<uint8_t>(ws, L.xq), at<uint8_t>(ws, L.xs),
-                        at<float>(ws, L.xg), s);
+                        at<float>(ws, L.xg), s, agx);
     record(events, 2 * MOE_STAGE_QUANT_X + 1, s);
     // 2. dispatch + tile list
     record(events, 2 * MOE_STAGE_DISPATCH, s);
@@ -390,9 +477,11 @@ static int forward_impl(const moe_config* c, const void* x, int32_t T, const int
   // 4. quantize h per (token, expert) row (NVFP4: the row scale needs the
   // whole row, so a kernel of its own; the row count lives on the device)
   record(events, 2 * MOE_STAGE_QUANT_H, s);
-  if (!fuse_h)
+  if (!fuse_h) {
+    if (agh.mode == 1) bad |= launch_act_gs_tensor(1, at<float>(ws, L.h), P, b.offsets + EL, F, ags, s);
     bad |= launch_quant(c->fmt, 1, at<float>(ws, L.h), P, b.offsets + EL, F, at<uint8_t>(ws, L.hq),
-                        at<uint8_t>(ws, L.hs), at<float>(ws, L.hg), s);
+                        at<uint8_t>(ws, L.hs), at<float>(ws, L.hg), s, agh);
+  }
   record(events, 2 * MOE_STAGE_QUANT_H + 1, s);
 
   // 5. down GEMM -> y (fp32, sorted rows)
@@ -418,6 +507,18 @@ int moe_forward_fused(const moe_config* c, const void* x, int32_t T, const int32
                       const float* topk_w, const moe_expert_weights* w, void* out, void* ws, size_t ws_bytes,
                       void* stream, void* const* events) {
   return forward_impl(c, x, T, topk_ids, topk_w, w, out, ws, ws_bytes, stream, events, true);
+}
+
+int moe_forward_fused_status(const moe_config* c, int32_t T, const void* ws, size_t ws_bytes, int32_t* err,
+                             void* stream) {
+  int st = moe_validate_config(c);
+  if (st != MOE_OK) return st;
+  if (T < 0 || err == nullptr || !aligned(err, 4)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(c, T, const_cast<void*>(ws), ws_bytes)) != MOE_OK) return st;
+  if ((st = device_check()) != MOE_OK) return st;
+  const Layout L = layout(c, c->max_tokens);
+  const int32_t* ctl = fused_applies(c, T) ? at<int32_t>(const_cast<void*>(ws), L.ctl) : nullptr;
+  return launch_fused_status(ctl, err, static_cast<hipStream_t>(stream)) == 0 ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
 }  // extern "C"

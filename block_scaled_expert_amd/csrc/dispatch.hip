@@ -239,7 +239,7 @@ __global__ __launch_bounds__(1024) void k_disp_small(const int32_t* __restrict__
 // Small batches, one launch for two independent steps of the forward:
 // workgroup 0 dispatches the pairs, workgroups 1.. quantize the bf16 token
 // rows (4 rows each, one per group of 256 threads).
-template <int FMT>
+template <int FMT, int GSM>
 __global__ __launch_bounds__(1024) void k_prep_small(const uint16_t* __restrict__ x, int T, int H,
                                                      uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
                                                      float* __restrict__ xg, const int32_t* __restrict__ ids,
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(1024) void k_prep_small(const uint16_t* __restrict_
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
                                                      int32_t* __restrict__ pos, int32_t* __restrict__ worklist,
                                                      int32_t* __restrict__ ntiles, int32_t* __restrict__ zero,
-                                                     int nzero) {
+                                                     int nzero, const float* __restrict__ gs_in, float gs_val) {
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i < nzero; i += 1024) zero[i] = 0;
     disp_small_body(ids, P, E_begin, E_local, tile_m, offsets, sorted, pos, worklist, ntiles);
@@ -260,24 +260,30 @@ __global__ __launch_bounds__(1024) void k_prep_small(const uint16_t* __restrict_
   const int rr = live ? row : T - 1;   // every group takes the barrier; only live rows write
   const uint16_t* xr = x + (size_t)rr * H;
   if (FMT == 1)
-    quant_row_nvfp4<uint16_t>(xr, H, t, red[grp], live, xq + (size_t)rr * (H / 2), xs + (size_t)rr * (H / 16),
-                              xg + rr);
+    quant_row_nvfp4<uint16_t, GSM>(xr, H, t, red[grp], live, xq + (size_t)rr * (H / 2), xs + (size_t)rr * (H / 16),
+                                   xg + rr, gs_in, gs_val);
   else
     quant_row_mxfp8<uint16_t>(xr, H, t, live, xq + (size_t)rr * H, xs + (size_t)rr * (H / 32));
 }
 
 int launch_prep_small(int fmt, const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs, float* xg,
                       const int32_t* ids, int P, int E_begin, int E_local, int tile_m, const DispatchBufs& b,
-                      int32_t* zero, int nzero, hipStream_t stream) {
+                      int32_t* zero, int nzero, hipStream_t stream, const ActGs& ag) {
   if (P > kSmallP || T <= 0) return -1;
   if (zero == nullptr) nzero = 0;
   const dim3 grid(1 + ceil_div(T, 4));
-  if (fmt == 1)
-    hipLaunchKernelGGL(k_prep_small<1>, grid, dim3(1024), 0, stream, x, T, H, xq, xs, xg, ids, P, E_begin, E_local,
-                       tile_m, b.offsets, b.sorted, b.pos, b.worklist, b.ntiles, zero, nzero);
-  else
-    hipLaunchKernelGGL(k_prep_small<2>, grid, dim3(1024), 0, stream, x, T, H, xq, xs, xg, ids, P, E_begin, E_local,
-                       tile_m, b.offsets, b.sorted, b.pos, b.worklist, b.ntiles, zero, nzero);
+#define MOE_PREP(F, M)                                                                                             \
+  hipLaunchKernelGGL((k_prep_small<F, M>), grid, dim3(1024), 0, stream, x, T, H, xq, xs, xg, ids, P, E_begin,   \
+                     E_local, tile_m, b.offsets, b.sorted, b.pos, b.worklist, b.ntiles, zero, nzero, ag.gs_dev, \
+                     ag.gs_val)
+  if (fmt == 1) {
+    if (ag.mode == GS_TENSOR) MOE_PREP(1, GS_TENSOR);
+    else if (ag.mode == GS_STATIC) MOE_PREP(1, GS_STATIC);
+    else MOE_PREP(1, GS_ROW);
+  } else {
+    MOE_PREP(2, GS_ROW);
+  }
+#undef MOE_PREP
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

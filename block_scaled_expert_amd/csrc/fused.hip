@@ -142,14 +142,43 @@ __global__ __launch_bounds__(256) void k_moe_fused(GemmArgs g, GemmArgs d, Fused
     if (tid == 0) atomic_add_relaxed(ctl + kCtlDownDone, 1);
   } else {
     const int i3 = item - n1 - n2, t = i3 / ncb, cb = i3 - t * ncb;
-    if (tid == 0) wait_at_least(ctl + kCtlDownDone, n2, ctl + kCtlErr);
+    if (tid == 0) {
+      wait_at_least(ctl + kCtlDownDone, n2, ctl + kCtlErr);
+      // a wait that ran out anywhere (a down item's included: it set the
+      // word before its count, whose stores completed first) poisons the sum
+      s_last = __hip_atomic_load(ctl + kCtlErr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     const int c = cb * 256 + tid;
-    if (c < H / 4) combine_col4<false>(f.y, f.pos, f.topk_w, g.k, H, f.out, t, c);
+    if (c < H / 4) {
+      if (__builtin_amdgcn_readfirstlane(s_last) == 0)
+        combine_col4<false>(f.y, f.pos, f.topk_w, g.k, H, f.out, t, c);
+      else
+        reinterpret_cast<uint2*>(f.out + (size_t)t * H)[c] = make_uint2(0x7FC07FC0u, 0x7FC07FC0u);
+    }
   }
 }
 
 int fused_ctl_words(int max_tiles) { return kCtlFixed + 2 * max_tiles; }
+
+namespace {
+
+// *dst = src ? *src : v (one thread).
+__global__ void k_put_word(int32_t* __restrict__ dst, const int32_t* __restrict__ src, int32_t v) {
+  *dst = src != nullptr ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : v;
+}
+
+}  // namespace
+
+int launch_fused_status(const int32_t* ctl, int32_t* err, hipStream_t stream) {
+  hipLaunchKernelGGL(k_put_word, dim3(1), dim3(1), 0, stream, err, ctl != nullptr ? ctl + kCtlErr : nullptr, 0);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_fused_force_error(int32_t* ctl, hipStream_t stream) {
+  hipLaunchKernelGGL(k_put_word, dim3(1), dim3(1), 0, stream, ctl + kCtlErr, nullptr, 1);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 namespace {
 

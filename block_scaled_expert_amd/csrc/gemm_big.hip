@@ -551,16 +551,16 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
   const int cl = lane & 15, g4 = lane >> 4;
   if (STAGE == 0) {
     const float inv_c = 1.0f / a.cap;
-    const float wg = a.w_gs[3 * el + 0], wu = a.w_gs[3 * el + 1];
+    const ScalePair wg = split_scale(a.w_gs[3 * el + 0]), wu = split_scale(a.w_gs[3 * el + 1]);
     const int col = bx * 128 + 16 * wave + cl;
     float h[4 * NSUB], u[4 * NSUB];
 #pragma unroll
     for (int i = 0; i < NSUB; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const float ga = rgs[16 * i + 4 * g4 + q];
-        h[4 * i + q] = (acc[i][0][q] * ga) * wg;
-        u[4 * i + q] = (acc[i][1][q] * ga) * wu;
+        const ScalePair ga = split_scale(rgs[16 * i + 4 * g4 + q]);
+        h[4 * i + q] = apply_scale(acc[i][0][q], ga * wg);
+        u[4 * i + q] = apply_scale(acc[i][1][q], ga * wu);
       }
     cap_swiglu_n(h, u, a.cap_form, a.cap, inv_c);
 #pragma unroll
@@ -572,17 +572,17 @@ __device__ __forceinline__ void big_nv_tile(const GemmArgs& a, const BigItem& it
         a.out[(size_t)(row0 + m) * a.F + col] = h[4 * i + q];
       }
   } else {
-    const float wd = a.w_gs[3 * el + 2];
+    const ScalePair wd = split_scale(a.w_gs[3 * el + 2]);
 #pragma unroll
     for (int i = 0; i < NSUB; i++)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const int m = 16 * i + 4 * g4 + q;
         if (m >= rows) continue;
-        const float ha = rgs[m];
+        const ScalePair hs = split_scale(rgs[m]) * wd;
 #pragma unroll
         for (int c = 0; c < 2; c++)
-          put_out(a, (size_t)(row0 + m) * a.H + bx * BNW + 32 * wave + 16 * c + cl, (acc[i][c][q] * ha) * wd);
+          put_out(a, (size_t)(row0 + m) * a.H + bx * BNW + 32 * wave + 16 * c + cl, apply_scale(acc[i][c][q], hs));
       }
   }
 }

@@ -343,9 +343,9 @@ __device__ __forceinline__ void expert_tile(const GemmArgs& a, int tile, int bx,
       const bool live = m < rows;
       float gv = ksum(m, c), uv = ksum(m, 32 + c);
       if (FMT == 1) {
-        const float ga = rgs[m];
-        gv = (gv * ga) * a.w_gs[3 * el + 0];
-        uv = (uv * ga) * a.w_gs[3 * el + 1];
+        const ScalePair ga = split_scale(rgs[m]);
+        gv = apply_scale(gv, ga * split_scale(a.w_gs[3 * el + 0]));
+        uv = apply_scale(uv, ga * split_scale(a.w_gs[3 * el + 1]));
       }
       const float h = cap_swiglu(gv, uv, a.cap_form, a.cap, inv_c);
       if (FMT == 2) {
@@ -367,7 +367,7 @@ __device__ __forceinline__ void expert_tile(const GemmArgs& a, int tile, int bx,
       const int m = idx >> 6, c = idx & 63;
       if (m >= rows) continue;
       float yv = ksum(m, c);
-      if (FMT == 1) yv = (yv * rgs[m]) * a.w_gs[3 * el + 2];
+      if (FMT == 1) yv = apply_scale(yv, split_scale(rgs[m]) * split_scale(a.w_gs[3 * el + 2]));
       st<COH>(a.out + (size_t)(row0 + m) * a.H + bx * BN + c, yv);
     }
   }

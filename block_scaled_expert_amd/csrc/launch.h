@@ -9,10 +9,28 @@
 
 namespace moe {
 
+// Where NVFP4 activation rows take their fp32 scale (enum moe_act_gs):
+// mode 0 per row; 1 the tensor's shared scale in the device word gs_dev
+// (launch_act_gs_tensor writes it); 2 the fixed value gs_val.
+struct ActGs {
+  int mode = 0;
+  const float* gs_dev = nullptr;
+  float gs_val = 1.0f;
+};
+
 // Activation quantization of `rows` rows (further limited by *rows_dev when
-// non-null) of width `cols`.  fmt: 1 NVFP4, 2 MXFP8.  dtype: 0 bf16, 1 fp32.
+// non-null) of width `cols`.  fmt: 1 NVFP4, 2 MXFP8 (ag ignored).  dtype: 0
+// bf16, 1 fp32.
 int launch_quant(int fmt, int dtype, const void* x, int rows, const int* rows_dev, int cols,
-                 uint8_t* codes, uint8_t* scales, float* gs, hipStream_t stream);
+                 uint8_t* codes, uint8_t* scales, float* gs, hipStream_t stream, const ActGs& ag = ActGs{});
+
+// The shared NVFP4 scale of a whole [rows][cols] tensor (rows limited by
+// *rows_dev when non-null): scratch[0] = max|x| / 2688 (1 for an all-zero
+// tensor), with scratch[1 .. 1 + kActGsPartials) holding partial maxima.
+constexpr int kActGsPartials = 256;
+constexpr size_t kActGsScratchBytes = 4 * (1 + kActGsPartials);
+int launch_act_gs_tensor(int dtype, const void* x, int rows, const int* rows_dev, int cols, float* scratch,
+                         hipStream_t stream);
 
 // Router: logits into z (fp32 workspace: router_splits(T, E) partial [T][E]
 // planes, router_z_rows(max_tokens) * E floats at most), then sigmoid + bias
@@ -44,7 +62,7 @@ constexpr int kSmallDispatchPairs = 4096;
 // zero (nullable): nzero int32 words the launch also clears.
 int launch_prep_small(int fmt, const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs, float* xg,
                       const int32_t* ids, int P, int E_begin, int E_local, int tile_m, const DispatchBufs& b,
-                      int32_t* zero, int nzero, hipStream_t stream);
+                      int32_t* zero, int nzero, hipStream_t stream, const ActGs& ag = ActGs{});
 
 // Weight encoding: nmat matrices [rows][cols] (dtype 0 bf16, 1 fp32) to
 // canonical NVFP4 (fmt 1: one fp32 scale per matrix, written to
@@ -121,6 +139,13 @@ struct FusedArgs {
 };
 int fused_ctl_words(int max_tiles);
 int launch_moe_fused(const GemmArgs& g, const GemmArgs& d, const FusedArgs& f, hipStream_t stream);
+// *err = the single launch's error word (ctl non-null) or 0 (ctl null)
+int launch_fused_status(const int32_t* ctl, int32_t* err, hipStream_t stream);
+// sets the error word (after the launch that clears it): every wait returns at once
+int launch_fused_force_error(int32_t* ctl, hipStream_t stream);
+
+// The epilogue's capped SwiGLU on n fp32 pairs (moe_cap_swiglu).
+int launch_cap_swiglu(int form, float cap, const float* g, const float* u, long n, float* h, hipStream_t stream);
 
 // Repack nmat canonical [N][K] matrices (codes + scales) into the packed
 // tile layout (moe_prepare_weights).

@@ -158,6 +158,24 @@ __device__ inline float wave_sum(float v) {
 
 __device__ inline float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// Two fp32 scale factors applied together: v * a * b as
+// ldexp(v * (mant(a) * mant(b)), exp(a) + exp(b)), mant in [0.5, 1).  A
+// token's activation scale and an expert's weight scale can each lie far
+// outside the range of their product with v (a row of 2^60-sized values has
+// an NVFP4 scale near 2^50), so multiplying them in one after the other can
+// overflow or underflow on the way; here only the final result can.  Two
+// roundings, like the two products it replaces; frexp / ldexp are single
+// instructions.
+struct ScalePair {
+  float m;
+  int e;
+};
+__device__ inline ScalePair split_scale(float a) {
+  return ScalePair{__builtin_amdgcn_frexp_mantf(a), __builtin_amdgcn_frexp_expf(a)};
+}
+__device__ inline ScalePair operator*(ScalePair a, ScalePair b) { return ScalePair{a.m * b.m, a.e + b.e}; }
+__device__ inline float apply_scale(float v, ScalePair s) { return __builtin_amdgcn_ldexpf(v * s.m, s.e); }
+
 // Reciprocal from the hardware instruction (v_rcp_f32, within 1 ulp; 1/inf
 // is 0).  The epilogues take their quotients this way: an IEEE division
 // expands to about ten instructions, which in the large-M gate/up epilogue
@@ -165,10 +183,17 @@ __device__ inline float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); 
 __device__ inline float rcp_fast(float y) { return __builtin_amdgcn_rcpf(y); }
 
 // tanh from one hardware exponential: tanh|x| = 1 - 2 / (e^{2|x|} + 1)
-// (relative error a few 1e-7; e^{2|x|} = inf gives exactly 1).
+// (e^{2|x|} = inf gives exactly 1).  That difference cancels as |x| -> 0
+// (its relative error grows like 1e-7 / |x|), so below |x| = 1/8 the odd
+// Taylor series to x^7 is used instead (truncation below 2e-9 relative).
+// Relative error: below about 2e-6 everywhere, measured against float64.
 __device__ inline float tanh_fast(float x) {
-  const float e = __expf(2.0f * fabsf(x));
-  return copysignf(1.0f - 2.0f * rcp_fast(e + 1.0f), x);
+  const float a = fabsf(x);
+  const float e = __expf(2.0f * a);
+  const float big = 1.0f - 2.0f * rcp_fast(e + 1.0f);
+  const float a2 = a * a;
+  const float small = a * (1.0f + a2 * (-1.0f / 3.0f + a2 * (2.0f / 15.0f + a2 * (-17.0f / 315.0f))));
+  return copysignf(a < 0.125f ? small : big, x);
 }
 
 // Cap + SwiGLU on fp32 gate/up values (cap forms of enum moe_cap_form).

@@ -80,25 +80,45 @@ __device__ inline uint32_t nvfp4_block(const float* v, float gs, float denom, bo
   return zero_row ? 0u : sc;
 }
 
+// Where an NVFP4 row takes its fp32 scale (enum moe_act_gs): computed from
+// the row (GS_ROW), read from one device word shared by the whole tensor
+// (GS_TENSOR, written by k_act_gs_finish), or a kernel argument (GS_STATIC).
+constexpr int GS_ROW = 0, GS_TENSOR = 1, GS_STATIC = 2;
+
+// fp32 scale of an NVFP4 scale domain with maximum A: A / 2688 (one IEEE
+// fp32 division; 2688 = 6 * 448), 1 for an all-zero domain.
+__device__ inline float nvfp4_gs(float A) { return A == 0.0f ? 1.0f : __fdiv_rn(A, 2688.0f); }
+
 // NVFP4 row of `cols` elements: codes (cols/2 bytes), E4M3 block scales
 // (cols/16) and the fp32 row scale.  live == false: the row is read and the
-// barrier taken, nothing is written.
-template <typename InT>
+// barrier taken, nothing is written.  MODE GS_ROW takes the row's own scale
+// (and a workgroup barrier: every thread must call it); GS_TENSOR reads
+// *gs_in; GS_STATIC uses gs_val (no barrier in either).
+template <typename InT, int MODE = GS_ROW>
 __device__ inline void quant_row_nvfp4(const InT* __restrict__ xr, int cols, int t, float* red, bool live,
                                        uint8_t* __restrict__ cr, uint8_t* __restrict__ sr,
-                                       float* __restrict__ gs_out) {
+                                       float* __restrict__ gs_out, const float* gs_in = nullptr,
+                                       float gs_val = 1.0f) {
 #pragma clang fp contract(off)
   const int nblk = cols / 16;
-  float A = 0.0f;
-  for (int b = t; b < nblk; b += 256) {
-    float v[16];
-    load_block<InT>(xr + 16 * b, 16, v);
+  bool zero_row = false;
+  float gs;
+  if constexpr (MODE == GS_ROW) {
+    float A = 0.0f;
+    for (int b = t; b < nblk; b += 256) {
+      float v[16];
+      load_block<InT>(xr + 16 * b, 16, v);
 #pragma unroll
-    for (int i = 0; i < 16; i++) A = fmaxf(A, fabsf(v[i]));
+      for (int i = 0; i < 16; i++) A = fmaxf(A, fabsf(v[i]));
+    }
+    A = group_max(A, red, t);
+    zero_row = (A == 0.0f);
+    gs = nvfp4_gs(A);
+  } else if constexpr (MODE == GS_TENSOR) {
+    gs = *gs_in;
+  } else {
+    gs = gs_val;
   }
-  A = group_max(A, red, t);
-  const bool zero_row = (A == 0.0f);
-  const float gs = zero_row ? 1.0f : __fdiv_rn(A, 2688.0f);
   const float denom = __fmul_rn(6.0f, gs);
   if (t == 0 && live) *gs_out = gs;
 

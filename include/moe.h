@@ -27,6 +27,11 @@
  *    as the pages' ROCm recipes accept gfx950 only (SGLang cookbook section
  *    2, "AMD").
  *  - Inputs are assumed finite.
+ *  - Alignment: bf16 activation and output arrays (x, out) and the expert
+ *    code arrays (w13, w2) must be 16-byte aligned, as must the quantized
+ *    codes of moe_quantize_act; fp32, int32 and scale arrays 4-byte aligned;
+ *    the workspace 256-byte aligned.  A misaligned pointer is
+ *    MOE_ERR_INVALID_ARG.
  *  - The library is stateless apart from a per-device architecture check
  *    cached on first use; calls on different streams do not share state
  *    except through the caller's buffers.
@@ -82,6 +87,17 @@ enum moe_cap_form {
 /* Enqueue values for moe_dtype arguments. */
 enum moe_dtype { MOE_DTYPE_BF16 = 0, MOE_DTYPE_F32 = 1 };
 
+/* Where NVFP4 activation rows (x for the gate/up GEMM, h for the down GEMM)
+ * take their fp32 scale.  The pages require only that it span each expert's
+ * full input width (SGLang cookbook "Inkling-2-Small", section 2,
+ * "Parallelism"); which of these the checkpoint uses is not stated.
+ *  PER_ROW:    each row its own, max|row| / 2688 (the default).
+ *  PER_TENSOR: one for the whole tensor of the call, max / 2688 over all T
+ *              x rows, and over all local (token, expert) h rows.
+ *  STATIC:     the fixed values act_gs_static[0] (x) and [1] (h).
+ * MXFP8 carries no fp32 scale and ignores this field. */
+enum moe_act_gs { MOE_ACT_GS_PER_ROW = 0, MOE_ACT_GS_PER_TENSOR = 1, MOE_ACT_GS_STATIC = 2 };
+
 /* Layer configuration (host struct, read during the call only). */
 typedef struct moe_config {
   int32_t hidden;             /* H: 4608 for Inkling 2 Small; multiple of 128 */
@@ -99,6 +115,9 @@ typedef struct moe_config {
   int32_t norm_topk;          /* 1: gate weights divided by their sum over k */
   float routed_scale;         /* gate weights multiplied by this (1.0) */
   int32_t max_tokens;         /* largest T the workspace is sized for */
+  int32_t act_gs;             /* enum moe_act_gs (NVFP4 activations) */
+  float act_gs_static[2];     /* MOE_ACT_GS_STATIC: positive finite fp32
+                                 scales of x and of h (at most 2^120) */
 } moe_config;
 
 /* Byte order of the expert weight arrays. */
@@ -153,27 +172,48 @@ int moe_check_arch(const char* arch);
 int moe_validate_config(const moe_config* cfg);
 
 /* Bytes of workspace moe_route, moe_dispatch, moe_forward and
- * moe_forward_fused need for up to cfg->max_tokens tokens.  Host only;
- * *bytes is a host pointer.  The workspace needs no initial contents: every
- * call writes what it later reads (moe_forward_fused's control words are
- * cleared by its own first launch). */
+ * moe_forward_fused need for up to cfg->max_tokens tokens: the library's
+ * counterpart of the per-rank token buffer that bounds one MoE forward
+ * (SGLang cookbook "Inkling-2-Small", section 2, "MegaMoE": a buffer sized
+ * for 4096 tokens per rank).  It holds the router's partial logits, the
+ * quantized tokens, the dispatch, and the intermediate h and y rows of every
+ * (token, expert) pair.  Host only; *bytes is a host pointer.  The
+ * workspace needs no initial contents: every call writes what it later
+ * reads (moe_forward_fused's control words are cleared by its own first
+ * launch). */
 int moe_workspace_size(const moe_config* cfg, size_t* bytes);
 
-/* Per-row activation quantization (the W4A4 / W8A8 step; Miles docs section
- * 5.3).  x: [rows][cols] bf16 (dtype MOE_DTYPE_BF16) or fp32.  cols must be
- * a multiple of 32.
+/* Activation quantization in cfg->fmt (the W4A4 / W8A8 step; Miles docs
+ * section 5.3).  x: [rows][cols] bf16 (dtype MOE_DTYPE_BF16) or fp32; cols
+ * a multiple of 32.  site: 0 for the gate/up input x, 1 for the down input
+ * h (selects act_gs_static[site]).
  *  NVFP4: codes [rows][cols/2], scales [rows][cols/16] E4M3, row_gs [rows]
- *         fp32.  Per row: A = max|v|; gs = A/2688 (1 if A == 0); per block
- *         of 16: s = E4M3(a_b / (6 gs)), codes E2M1(v * (1 / (s gs))), all
- *         in IEEE fp32, round to nearest even, saturating; a zero scale
- *         zeroes its block.  The fp32 scale spans the row's full width
- *         (SGLang cookbook section 2, "Parallelism").
+ *         fp32.  Row scale gs per cfg->act_gs: PER_ROW A = max|row|, gs =
+ *         A/2688 (1 and an all-zero row if A == 0); PER_TENSOR the same
+ *         over all rows (every row_gs entry then holds it); STATIC
+ *         act_gs_static[site].  Per block of 16: s = E4M3(a_b / (6 gs)),
+ *         codes E2M1(v * (1 / (s gs))), all in IEEE fp32, round to nearest
+ *         even, saturating; a zero scale zeroes its block.  The fp32 scale
+ *         spans the row's full width (SGLang cookbook section 2,
+ *         "Parallelism").
  *  MXFP8: codes [rows][cols], scales [rows][cols/32] E8M0, row_gs unused.
  *         Per block of 32: X = 2^(floor(log2 amax) - 8) (2^-127 for a zero
  *         block), codes E4M3(v / X) saturating.
- * The result is bit-identical to the definition above. */
-int moe_quantize_act(int32_t fmt, int32_t dtype, const void* x, int32_t rows, int32_t cols,
-                     uint8_t* codes, uint8_t* scales, float* row_gs, void* stream);
+ * ws: device scratch of at least 1028 bytes, 4-byte aligned, for NVFP4 with
+ * PER_TENSOR (two passes: partial maxima, then the shared scale); unused
+ * (may be NULL) otherwise.  The result is bit-identical to the definition
+ * above. */
+int moe_quantize_act(const moe_config* cfg, int32_t site, int32_t dtype, const void* x, int32_t rows,
+                     int32_t cols, uint8_t* codes, uint8_t* scales, float* row_gs, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* The capped SwiGLU of the expert epilogue on n fp32 (gate, up) pairs:
+ * h[i] = cap form cfg->cap_form with c = cfg->cap applied to (g[i], u[i])
+ * (enum moe_cap_form), evaluated with the same device arithmetic as the
+ * gate/up GEMMs' epilogues (hardware exponential and reciprocal; tanh from
+ * an odd series below |x| = 1/8).  Arrays 4-byte aligned, n >= 0.  Lets a
+ * caller measure the epilogue's error against an exact evaluation. */
+int moe_cap_swiglu(const moe_config* cfg, const float* g, const float* u, int64_t n, float* h, void* stream);
 
 /* moe_encode_weights: expert weight matrices to the checkpoint formats on
  * the GPU, with every scale recomputed from the data -- what a weight sync
@@ -284,18 +324,32 @@ int moe_forward(const moe_config* cfg, const void* x, int32_t T, const int32_t* 
  * one kernel runs gate/up + capped SwiGLU, h quantization, down and the
  * combine as work items, one workgroup each, in the order a device-side
  * counter hands them out; an item waits only on items before it, so the
- * launch drains whatever the number of resident workgroups.  Each wait is also bounded (about a second of
- * polling; reaching the bound needs a device fault elsewhere): a wait that
- * runs out sets an error word in the workspace, every later wait returns at
- * once, the launch completes and `out` is undefined.  Same arguments, workspace,
+ * launch drains whatever the number of resident workgroups.  Each wait is
+ * also bounded (about a second of polling; reaching the bound needs a device
+ * fault elsewhere): a wait that runs out sets an error word in the
+ * workspace, every later wait returns at once, the launch completes and the
+ * combine writes bf16 NaN instead of sums (moe_forward_fused_status reads
+ * the word).  Same arguments, workspace,
  * result (bit-identical to moe_forward) and errors as moe_forward.  It
  * applies when T * top_k <= 4096 and the expected rows per local expert
  * (T * top_k / num_experts) are at most 48; other batches run moe_forward's
  * launch sequence.  events: the GATE_UP pair times the single launch;
- * the QUANT_H, DOWN and COMBINE pairs are recorded back to back after it. */
+ * the QUANT_H, DOWN and COMBINE pairs are recorded back to back after it.
+ * cfg->act_gs PER_TENSOR and STATIC run the launch sequence as well. */
 int moe_forward_fused(const moe_config* cfg, const void* x, int32_t T, const int32_t* topk_ids,
                       const float* topk_w, const moe_expert_weights* weights, void* out,
                       void* ws, size_t ws_bytes, void* stream, void* const* events);
+
+/* Status of the last moe_forward_fused call on workspace ws (same cfg and
+ * T): enqueues on `stream` a store of its error word to *err (device int32):
+ * 0 when every dependency wait of the single launch was met; 1 when one ran
+ * out of polls, in which case every combine item wrote bf16 NaN (0x7FC0) to
+ * its part of `out` instead of a sum.  For a (cfg, T) that ran moe_forward's
+ * launch sequence instead, *err is 0.  Setting the environment variable
+ * MOE_FUSED_TEST_FAIL to 1 makes moe_forward_fused start with the error word
+ * set (a test hook for this path: every wait then returns at once). */
+int moe_forward_fused_status(const moe_config* cfg, int32_t T, const void* ws, size_t ws_bytes, int32_t* err,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -279,7 +279,7 @@ def expert_forward(cfg: OracleConfig, xq64: np.ndarray, wdeq, h_gs=None):
 # --------------------------------------------------------------------------
 
 def moe_layer(cfg: OracleConfig, x_bf16, w_router_bf16, bias, expert_weights,
-              tokens=None, topk_ids=None, topk_w=None):
+              tokens=None, topk_ids=None, topk_w=None, workers: int = 1):
     """Plain definition of the layer.
 
     expert_weights: callable e -> dict (canonical layout of expert e), or a
@@ -287,6 +287,9 @@ def moe_layer(cfg: OracleConfig, x_bf16, w_router_bf16, bias, expert_weights,
     tokens: optional array of token indices; only those outputs are computed
     (the router still runs on those tokens only).
     topk_ids/topk_w: optional routing replay (replaces the router's choice).
+    workers: experts are independent, so with workers > 1 they are evaluated
+    by a pool of forked worker processes (the same arithmetic per expert;
+    results are placed by expert).
     Under act_gs "tensor" the x scale is taken over all T tokens even when
     `tokens` selects some; the h scale needs every local pair's h, so
     `tokens` must then be None.
@@ -312,12 +315,17 @@ def moe_layer(cfg: OracleConfig, x_bf16, w_router_bf16, bias, expert_weights,
     get = expert_weights if callable(expert_weights) else (lambda e: expert_weights[e - cfg.expert_begin])
     if not per_tensor:
         h_gs = act_scale(cfg, 1, None) if cfg.act_gs == "static" else None
+
+        jobs = []
         for e in cfg.local:                               # expert-index order
             rows, slots = np.nonzero(ids == e)
-            if rows.size == 0:
-                continue
-            wdeq = dequantize_expert(cfg.fmt, get(e))
-            ye, _ = expert_forward(cfg, xq[rows], wdeq, h_gs)
+            if rows.size:
+                jobs.append((rows, slots, (cfg, xq[rows], get, e, h_gs)))
+        if workers > 1 and len(jobs) > 1:
+            ys = _run_pool(workers, get, [j[2] for j in jobs])
+        else:
+            ys = [_expert_job(j[2]) for j in jobs]
+        for (rows, slots, _), ye in zip(jobs, ys):
             y[rows, slots] = ye
             have[rows, slots] = True
     else:
@@ -335,6 +343,30 @@ def moe_layer(cfg: OracleConfig, x_bf16, w_router_bf16, bias, expert_weights,
 
     out = combine(tw, y, have)
     return dict(out=out, route=r, topk_ids=ids, topk_w=tw, y=y, have=have, tokens=tok, x_gs=x_gs)
+
+
+def _expert_job(job):
+    """fp32 y of one expert's rows: job = (cfg, dequantized x rows, weight
+    source, e, shared h scale or None); the weight source is get(e) when
+    callable, else the expert's weights themselves."""
+    cfg, xr, src, e, h_gs = job
+    ew = src(e) if callable(src) else src
+    ye, _ = expert_forward(cfg, xr, dequantize_expert(cfg.fmt, ew), h_gs)
+    return ye
+
+
+def _run_pool(workers: int, get, jobs):
+    """_expert_job over jobs in forked worker processes.  A weight source
+    that cannot be pickled is resolved here and its arrays are sent."""
+    import multiprocessing
+    import pickle
+    from concurrent.futures import ProcessPoolExecutor
+    try:
+        pickle.dumps(get)
+    except Exception:
+        jobs = [(c, xr, get(e), e, g) for (c, xr, _, e, g) in jobs]
+    with ProcessPoolExecutor(workers, mp_context=multiprocessing.get_context("fork")) as ex:
+        return list(ex.map(_expert_job, jobs))
 
 
 def combine(tw: np.ndarray, y: np.ndarray, have: np.ndarray) -> np.ndarray:

@@ -7,7 +7,8 @@ function of (seed, stream, ...) through numpy's PCG64 with a SeedSequence, so
 any single expert can be regenerated on its own.
 
 Streams: 0 = tokens x, 1 = router weight, 2 = router bias, (3, e) = float
-weights of expert e, (4, e) = direct-code weights of expert e.
+weights of expert e, (4, e) = direct-code weights of expert e, (5, e) =
+edge-case direct-code weights of expert e.
 """
 from __future__ import annotations
 
@@ -132,10 +133,69 @@ def _nv_scales(g: np.random.Generator, shape) -> np.ndarray:
     return np.uint8(0x68) + (_bytes(g, shape) & np.uint8(0xF))
 
 
-def expert_direct_codes(seed: int, e: int, H: int, Fd: int, fmt: str, gain: float = 1.0) -> dict:
+# Edge-case direct codes (edge=True, stream (5, e)): scale and element codes
+# at the ends of their ranges, by expert e % 3:
+#   NVFP4  0: every block scale subnormal (E4M3 0x01..0x07) or, one in ten,
+#             zero; fp32 scales 2^-1 * U(0.9, 1.1) to keep the magnitudes
+#          1: block scales over every normal E4M3 exponent (0x08..0x7E), one
+#             in ten zero; fp32 scales 2^-20 * U(0.9, 1.1)
+#          2: the plain draw above, but one block scale in ten zero
+#   MXFP8  0: every element subnormal (exponent field 0) or zero, E8M0
+#             scales 2^-6 .. 2^-4
+#          1: elements over every exponent field, one in ten +-0, two in ten
+#             subnormal; E8M0 scales 2^-27 .. 2^-1
+#          2: the plain draw, one element in ten +-0
+
+
+def _edge_codes(g: np.random.Generator, e: int, H: int, Fd: int, fmt: str, gain: float) -> dict:
+    kind = e % 3
+    if fmt == "nvfp4":
+        def scales(shape):
+            b, c = _bytes(g, shape), _bytes(g, shape)
+            if kind == 0:
+                sc = np.uint8(1) + (b % np.uint8(7))
+            elif kind == 1:
+                sc = np.uint8(8) + (b % np.uint8(0x77))
+            else:
+                sc = np.uint8(0x68) + (b & np.uint8(0xF))
+            return np.where(c < 26, np.uint8(0), sc).astype(np.uint8)
+        base = {0: 2.0 ** -1, 1: 2.0 ** -20, 2: 2.0 ** -14}[kind]
+        w13, w13_sc = _bytes(g, (2 * Fd, H // 2)).copy(), scales((2 * Fd, H // 16))
+        w2, w2_sc = _bytes(g, (H, Fd // 2)).copy(), scales((H, Fd // 16))
+        gs = np.float32(base) * g.uniform(0.9, 1.1, size=3).astype(np.float32) * np.float32(gain)
+        return dict(w13=w13, w13_sc=w13_sc, w2=w2, w2_sc=w2_sc, gs=gs.astype(np.float32))
+
+    def elems(shape):
+        b, c = _bytes(g, shape), _bytes(g, shape)
+        sign = b & np.uint8(0x80)
+        if kind == 0:
+            mag = np.where(c < 26, np.uint8(0), np.uint8(1) + (b % np.uint8(7)))
+        elif kind == 1:
+            mag = np.where(c < 26, np.uint8(0),
+                           np.where(c < 77, np.uint8(1) + (b % np.uint8(7)), np.uint8(8) + (b % np.uint8(0x77))))
+        else:
+            mag = np.where(c < 26, np.uint8(0), np.minimum(np.uint8(0x50) | (b & np.uint8(0x2F)), np.uint8(0x7E)))
+        return (sign | mag).astype(np.uint8)
+
+    def e8(shape):
+        b = _bytes(g, shape)
+        lo, n = {0: (121, 3), 1: (100, 27), 2: (112, 3)}[kind]
+        return (np.uint8(lo) + (b % np.uint8(n))).astype(np.uint8)
+
+    return dict(w13=elems((2 * Fd, H)), w13_sc=e8((2 * Fd, H // 32)), w2=elems((H, Fd)), w2_sc=e8((H, Fd // 32)))
+
+
+def expert_direct_codes(seed: int, e: int, H: int, Fd: int, fmt: str, gain: float = 1.0,
+                        edge: bool = False) -> dict:
     """Canonical-layout weights of expert e drawn directly as codes.
     gain multiplies the fp32 (NVFP4) scales or shifts the E8M0 scales by
-    round(log2 gain) (MXFP8); it is used to push activations into the cap."""
+    round(log2 gain) (MXFP8); it is used to push activations into the cap.
+    edge: the edge-case draws described above (zero and subnormal scales and
+    elements)."""
+    if edge:
+        if fmt not in ("nvfp4", "mxfp8"):
+            raise ValueError(fmt)
+        return _edge_codes(rng(seed, 5, e), e, H, Fd, fmt, gain)
     g = rng(seed, 4, e)
     if fmt == "nvfp4":
         w13 = _bytes(g, (2 * Fd, H // 2)).copy()

@@ -41,6 +41,24 @@ def expert_weights(w: synth.Workload, e: int, gain: float = 1.0, sigma: float = 
     return synth.expert_direct_codes(w.seed, e, w.hidden, w.ffn, w.fmt, gain=gain)
 
 
+class ExpertSource:
+    """Picklable weight source for the oracle: e -> canonical weights of
+    expert e of workload w (what expert_weights returns), so the oracle's
+    worker processes draw their own experts."""
+
+    def __init__(self, w: synth.Workload, gain: float = 1.0, edge: bool = False):
+        self.w, self.gain, self.edge = w, gain, edge
+
+    def __call__(self, e: int) -> dict:
+        if self.edge:
+            return synth.expert_direct_codes(self.w.seed, e, self.w.hidden, self.w.ffn, self.w.fmt, gain=self.gain,
+                                             edge=True)
+        return expert_weights(self.w, e, self.gain)
+
+
+ORACLE_WORKERS = 8
+
+
 def stack_local(w: synth.Workload, gain: float = 1.0) -> dict:
     n = w.experts if w.num_local is None else w.num_local
     ews = [expert_weights(w, w.expert_begin + i, gain) for i in range(n)]

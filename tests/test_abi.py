@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("moe_route", "moe_quantize_act", "moe_forward", "moe_forward_fused", "moe_dispatch",
               "moe_prepare_weights", "moe_workspace_size", "moe_status_string", "moe_check_arch",
-              "moe_validate_config", "moe_encode_weights", "moe_decode_weights"):
+              "moe_validate_config", "moe_encode_weights", "moe_decode_weights", "moe_forward_fused_status",
+              "moe_cap_swiglu"):
         assert n in names
 
 
@@ -120,10 +121,15 @@ def test_host_checks_before_device(lib):
     assert lib.moe_forward_fused(ctypes.byref(cc), None, 0, None, None, None, None, ctypes.c_void_p(0x1000),
                                  n.value, None, None) == 0
     # bad quantize arguments
-    assert lib.moe_quantize_act(1, 0, None, 4, 48, None, None, None, None) == -1   # cols % 32
-    assert lib.moe_quantize_act(3, 0, None, 4, 64, None, None, None, None) == -5   # format
-    assert lib.moe_quantize_act(1, 2, None, 4, 64, None, None, None, None) == -1   # dtype
-    assert lib.moe_quantize_act(1, 0, None, 0, 64, None, None, None, None) == 0    # nothing to do
+    q = lib.moe_quantize_act
+    r = ctypes.byref(cc)
+    assert q(r, 0, 0, None, 4, 48, None, None, None, None, 0, None) == -1   # cols % 32
+    bad = _cfg().c()
+    bad.fmt = 3
+    assert q(ctypes.byref(bad), 0, 0, None, 4, 64, None, None, None, None, 0, None) == -5   # format
+    assert q(r, 0, 2, None, 4, 64, None, None, None, None, 0, None) == -1   # dtype
+    assert q(r, 2, 0, None, 4, 64, None, None, None, None, 0, None) == -1   # site
+    assert q(r, 0, 0, None, 0, 64, None, None, None, None, 0, None) == 0    # nothing to do
     # weights: bad layout value / canonical source required
     w = bse.CWeights(1, 1, 1, 1, 1, 5)
     assert lib.moe_prepare_weights(ctypes.byref(cc), ctypes.byref(w), ctypes.byref(bse.CWeights()), None) == -1
@@ -145,3 +151,63 @@ def test_encode_decode_host_checks(lib):
     assert dec(3, p, p, p, 1, 1, 2, 16, 64, p, None) == -5
     assert dec(1, p, p, None, 1, 1, 2, 16, 64, p, None) == -1
     assert dec(2, p, p, None, 1, 1, 0, 16, 64, p, None) == 0
+
+
+def test_act_gs_config(lib):
+    for kw, status in [({"act_gs": 0}, 0), ({"act_gs": 1}, 0), ({"act_gs": 2}, 0), ({"act_gs": 3}, -1),
+                       ({"act_gs": -1}, -1), ({"act_gs": 2, "act_gs_static": (0.0, 1.0)}, -1),
+                       ({"act_gs": 2, "act_gs_static": (1.0, float("nan"))}, -1),
+                       ({"act_gs": 2, "act_gs_static": (1.0, float("inf"))}, -1),
+                       ({"act_gs": 2, "act_gs_static": (1.0, 2.0 ** 121)}, -1),
+                       ({"act_gs": 2, "act_gs_static": (2.0 ** -100, 2.0 ** 120)}, 0),
+                       # MXFP8 carries no fp32 activation scale: the static values are not read
+                       ({"fmt": "mxfp8", "act_gs": 2, "act_gs_static": (0.0, 0.0)}, 0)]:
+        cc = _cfg(**kw).c()
+        assert lib.moe_validate_config(ctypes.byref(cc)) == status, kw
+    # per-tensor NVFP4 needs scratch for its two passes; the others do not
+    q = lib.moe_quantize_act
+    p = ctypes.c_void_p(0x1000)
+    cc = _cfg(act_gs=1).c()
+    assert q(ctypes.byref(cc), 0, 0, p, 4, 64, p, p, p, None, 0, None) == -1
+    assert q(ctypes.byref(cc), 0, 0, p, 4, 64, p, p, p, p, bse.ACT_GS_SCRATCH_BYTES - 1, None) == -3
+
+
+MISALIGNED = ctypes.c_void_p(0x1008)   # 8-byte aligned, not 16
+
+
+def test_alignment_checked_before_device(lib):
+    """Pointers the kernels read or write with 16-byte vector accesses are
+    rejected when misaligned, before anything is enqueued."""
+    cc = _cfg(max_tokens=64).c()
+    r = ctypes.byref(cc)
+    n = ctypes.c_size_t(0)
+    lib.moe_workspace_size(r, ctypes.byref(n))
+    ws, ok = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x2000)
+    # moe_quantize_act: x and codes 16-byte aligned, row_gs 4
+    q = lib.moe_quantize_act
+    assert q(r, 0, 0, MISALIGNED, 4, 64, ok, ok, ok, None, 0, None) == -1
+    assert q(r, 0, 0, ok, 4, 64, MISALIGNED, ok, ok, None, 0, None) == -1
+    assert q(r, 0, 0, ok, 4, 64, ok, ok, ctypes.c_void_p(0x2002), None, 0, None) == -1
+    # moe_route: x and the router weight 16, bias / ids / weights 4
+    rt = lib.moe_route
+    assert rt(r, MISALIGNED, 8, ok, ok, ok, ok, None, ws, n.value, None) == -1
+    assert rt(r, ok, 8, MISALIGNED, ok, ok, ok, None, ws, n.value, None) == -1
+    assert rt(r, ok, 8, ok, ctypes.c_void_p(0x2001), ok, ok, None, ws, n.value, None) == -1
+    # moe_forward / moe_forward_fused: x, out, w13, w2 16; scales, gs, ids, weights 4
+    good = bse.CWeights(0x4000, 0x5000, 0x6000, 0x7000, 0x8000, 1)
+    for fwd in (lib.moe_forward, lib.moe_forward_fused):
+        assert fwd(r, MISALIGNED, 8, ok, ok, ctypes.byref(good), ok, ws, n.value, None, None) == -1
+        assert fwd(r, ok, 8, ok, ok, ctypes.byref(good), MISALIGNED, ws, n.value, None, None) == -1
+        assert fwd(r, ok, 8, ctypes.c_void_p(0x2002), ok, ctypes.byref(good), ok, ws, n.value, None, None) == -1
+        for field, bad_ptr in (("w13", 0x4008), ("w2", 0x6008), ("w13_sc", 0x5002), ("w2_sc", 0x7001),
+                               ("gs", 0x8002)):
+            w = bse.CWeights(0x4000, 0x5000, 0x6000, 0x7000, 0x8000, 1)
+            setattr(w, field, bad_ptr)
+            assert fwd(r, ok, 8, ok, ok, ctypes.byref(w), ok, ws, n.value, None, None) == -1, field
+    # moe_cap_swiglu and moe_forward_fused_status: 4-byte aligned arrays
+    assert lib.moe_cap_swiglu(r, ctypes.c_void_p(0x2002), ok, 16, ok, None) == -1
+    assert lib.moe_cap_swiglu(r, ok, ok, -1, ok, None) == -1
+    assert lib.moe_cap_swiglu(r, None, None, 0, None, None) == 0
+    assert lib.moe_forward_fused_status(r, 8, ws, n.value, ctypes.c_void_p(0x2002), None) == -1
+    assert lib.moe_forward_fused_status(r, 8, ws, n.value - 1, ok, None) == -3
+    assert lib.moe_forward_fused_status(r, 65, ws, n.value, ok, None) == -4

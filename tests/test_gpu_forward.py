@@ -17,11 +17,16 @@ from _util import OUT_RTOL, inputs, lib_cfg, oracle_cfg, rel_err, stack_local, t
 pytestmark = pytest.mark.gpu
 
 
-def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None, layout="packed", fused=False):
+def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None, layout="packed", fused=False, act=None,
+              expect_fused_err=0):
+    """act: optional (act_gs mode, (x scale, h scale)) for NVFP4 activations.
+    fused: moe_forward_fused, whose status word must equal expect_fused_err."""
     import torch
     x, wr, b = inputs(w, T)
     T = x.shape[0]
     kw = {} if cap_form is None else {"cap_form": cap_form}
+    if act is not None:
+        kw.update(act_gs=act[0], act_gs_static=act[1])
     cfg = lib_cfg(bse, w, max_tokens=max_tokens or T, **kw)
     stacked, ews = stack_local(w, gain)
     wd = {k: to_dev(v) for k, v in stacked.items()}
@@ -36,13 +41,24 @@ def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None, layout="
     out = torch.empty((T, w.hidden), dtype=torch.bfloat16, device="cuda")
     bse.route(cfg, xt, wrt, torch.from_numpy(b).cuda(), ids, tw, nt, ws)
     bse.forward(cfg, xt, ids, tw, wd, out, ws, fused=fused)
+    fused_err = None
+    if fused:   # the single launch's error word: every dependency wait met
+        err = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        bse.forward_fused_status(cfg, T, ws, err)
+        fused_err = int(err.cpu().item())
+        assert fused_err == expect_fused_err
     torch.cuda.synchronize()
     return dict(x=x, wr=wr, b=b, ids=ids.cpu().numpy(), tw=tw.cpu().numpy(),
-                out=out.view(torch.int16).cpu().numpy().view(np.uint16), ews=ews)
+                out=out.view(torch.int16).cpu().numpy().view(np.uint16), ews=ews, fused_err=fused_err)
 
 
-def oracle_out(w, r, tokens=None, gain=1.0, cap_form=None):
+ACT_NAMES = {0: "row", 1: "tensor", 2: "static"}
+
+
+def oracle_out(w, r, tokens=None, gain=1.0, cap_form=None, act=None):
     kw = {} if cap_form is None else {"cap_form": cap_form}
+    if act is not None:
+        kw.update(act_gs=ACT_NAMES[act[0]], act_gs_static=tuple(np.float32(v) for v in act[1]))
     cfg = oracle_cfg(w, **kw)
     if r.get("ews") is not None:
         ew = r["ews"]
@@ -118,8 +134,10 @@ def test_single_token_and_max_tokens_margin(gpu_lib):
     assert rel_err(r["out"], oracle_out(w, r)) <= OUT_RTOL
 
 
-@pytest.mark.parametrize("key,ntok", [("decode_nvfp4", 3), ("decode_mxfp8", 3), ("ep8_mxfp8", 3),
-                                      ("prefill_nvfp4", 2)])
+# The decode batches and the EP share are compared on every token in
+# test_gpu_parity_full.py; the whole prefill chunk (whose y exceeds the
+# last-level cache and streams) on sampled tokens here.
+@pytest.mark.parametrize("key,ntok", [("prefill_nvfp4", 2)])
 def test_inkling_workloads_sampled(gpu_lib, key, ntok):
     w = synth.WORKLOADS[key]
     r = run_layer(gpu_lib, w)
@@ -148,3 +166,27 @@ def test_packed_layout_matches_canonical_bit_exact(gpu_lib, key):
     b = run_layer(gpu_lib, w, layout="packed")
     assert np.array_equal(a["ids"], b["ids"])
     assert np.array_equal(a["out"], b["out"])
+
+
+# NVFP4 activation scales per tensor and static (the alternatives of the
+# per-row reading): the one-launch quantize + dispatch (<= 4096 pairs, 32-row
+# entries), the large-M kernels (128-row entries) and the general dispatch
+# (more than 4096 pairs), every token against the oracle.
+ACT_CASES = {
+    "mid_nvfp4": SMALL["mid_nvfp4"],
+    "many_rows": SMALL["many_rows"],
+    "pairs_over_4096": synth.Workload("pairs_over_4096", "general dispatch", 600, 256, 128, 8, 128, "nvfp4", 44,
+                                      weights="gaussian"),
+}
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("key", list(ACT_CASES))
+def test_nvfp4_shared_activation_scales(gpu_lib, key, mode):
+    w = ACT_CASES[key]
+    act = (mode, (4.0 / 2688, 0.25 / 2688))
+    r = run_layer(gpu_lib, w, act=act)
+    ref = oracle_out(w, r, act=act)
+    assert rel_err(r["out"], ref) <= OUT_RTOL
+    # the shared scales change the result (they are not the per-row ones)
+    assert not np.array_equal(ref, oracle_out(w, r))

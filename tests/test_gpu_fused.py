@@ -115,3 +115,30 @@ def test_fused_cap_forms_under_stress(gpu_lib, form, fmt):
     b = run_layer(gpu_lib, w, gain=10.0, cap_form=form, fused=True)
     assert np.array_equal(a["out"], b["out"])
     assert rel_err(b["out"], oracle_out(w, b, cap_form=form)) <= OUT_RTOL
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_fused_with_shared_activation_scales_runs_the_sequence(gpu_lib, mode):
+    """Per-tensor and static NVFP4 activation scales: moe_forward_fused runs
+    moe_forward's launch sequence (bit-identical) and reports status 0."""
+    w = CASES["mid_nvfp4"]
+    act = (mode, (4.0 / 2688, 0.25 / 2688))
+    a = run_layer(gpu_lib, w, act=act)
+    b = run_layer(gpu_lib, w, act=act, fused=True)
+    assert np.array_equal(a["out"], b["out"]) and b["fused_err"] == 0
+
+
+def test_fused_error_word_poisons_the_output(gpu_lib, monkeypatch):
+    """The failure path of the bounded waits, forced from the host: with
+    MOE_FUSED_TEST_FAIL=1 the launch starts with its error word set, every
+    wait returns at once, the launch drains, every combine item writes bf16
+    NaN, and moe_forward_fused_status reports 1.  A later call without the
+    hook is clean again."""
+    w = CASES["mid_nvfp4"]
+    monkeypatch.setenv("MOE_FUSED_TEST_FAIL", "1")
+    bad = run_layer(gpu_lib, w, fused=True, expect_fused_err=1)
+    assert np.all(bad["out"] == 0x7FC0)
+    monkeypatch.delenv("MOE_FUSED_TEST_FAIL")
+    good = run_layer(gpu_lib, w, fused=True)
+    ref = run_layer(gpu_lib, w)
+    assert np.array_equal(good["out"], ref["out"])

@@ -97,3 +97,52 @@ def test_quantize_prefill_rows_bit_exact(gpu_lib):
         assert np.array_equal(gs[lo:lo + 4096].cpu().numpy(), g)
         assert np.array_equal(scales[lo:lo + 4096].cpu().numpy(), s)
         assert np.array_equal(codes[lo:lo + 4096].cpu().numpy(), c)
+
+
+def _shared_scale_case(gpu_lib, mode, x, dtype, site, H):
+    """GPU quantize_act with one scale for all rows vs the oracle's tensor /
+    static domains; returns nothing, asserts bit-identity."""
+    import torch
+    R = x.shape[0]
+    static = (np.float32(1.37 / 8), np.float32(0.0123))
+    cfg = gpu_lib.Config(fmt="nvfp4", act_gs=gpu_lib.ACT_GS_PER_TENSOR if mode == "tensor" else gpu_lib.ACT_GS_STATIC,
+                         act_gs_static=(float(static[0]), float(static[1])))
+    xt = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if dtype == "bf16" else torch.from_numpy(x)).cuda()
+    codes = torch.empty((R, H // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((R, H // 16), dtype=torch.uint8, device="cuda")
+    gs = torch.empty(R, dtype=torch.float32, device="cuda")
+    ws = torch.empty(gpu_lib.ACT_GS_SCRATCH_BYTES, dtype=torch.uint8, device="cuda")
+    gpu_lib.quantize_act(cfg, xt, codes, scales, gs, site=site, ws=ws if mode == "tensor" else None)
+    torch.cuda.synchronize()
+    xf = F.bf16_bits_to_f32(x) if dtype == "bf16" else x
+    if mode == "tensor":
+        c, s, g = F.quantize_nvfp4(xf, domain="tensor")
+    else:
+        c, s, g = F.quantize_nvfp4(xf, domain="static", gs=static[site])
+    assert np.array_equal(gs.cpu().numpy().view(np.uint32), np.full(R, g, np.float32).view(np.uint32))
+    assert np.array_equal(scales.cpu().numpy(), s)
+    assert np.array_equal(codes.cpu().numpy(), c)
+
+
+@pytest.mark.parametrize("site", [0, 1])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["tensor", "static"])
+def test_quantize_nvfp4_shared_scale_bit_exact(gpu_lib, mode, dtype, site):
+    """Per-tensor and static NVFP4 activation scales (the alternatives of the
+    per-row reading): codes, block scales and the shared fp32 scale
+    bit-identical to the oracle, including saturating rows."""
+    if dtype == "bf16":
+        H = 4608
+        x = np.concatenate([synth.tokens(5, 40, H), _edge_rows_bf16(H)])
+    else:
+        H = 2304
+        x = _f32_rows(H)
+    _shared_scale_case(gpu_lib, mode, x, dtype, site, H)
+
+
+def test_quantize_nvfp4_per_tensor_many_rows(gpu_lib):
+    """A tensor of 5000 Inkling-width rows: the two-pass maximum runs over 256
+    partial slices; one row holds the tensor maximum."""
+    x = synth.tokens(9, 5000, 4608)
+    x[3117, 100] = synth.to_bf16_bits(np.array([[-40.0]], np.float32))[0, 0]
+    _shared_scale_case(gpu_lib, "tensor", x, "bf16", 0, 4608)

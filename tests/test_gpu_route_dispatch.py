@@ -3,7 +3,9 @@
 Routing: the chosen expert sets must be identical for every token that is
 not a near tie (8th/9th selection-score gap >= 1e-6 on either side); for
 near ties the GPU's set must still be a valid top-k under the oracle's
-scores within the tie band.  Gate weights within 1e-5 relative.
+scores within the tie band.  The ids are listed in descending score (the
+oracle's order wherever no two chosen scores lie within the tie band).
+Gate weights within 1e-5 relative.
 Dispatch: offsets, sorted pair ids and pair positions bit-identical.
 """
 import numpy as np
@@ -42,8 +44,14 @@ def _check_route(w, x, wr, b, ids, tw, nt):
         assert len(gset) == k
         if not tie[t]:
             assert gset == oset, f"token {t}"
-            # same order as the oracle (descending score)
-            assert list(ids[t]) == list(r["topk_ids"][t]), f"token {t}"
+            # listed in descending score: the oracle's order, except between
+            # chosen experts whose scores lie within the tie band (fp32 sums
+            # in another order may swap those)
+            sel = r["sel"][t].astype(np.float64)
+            assert all(sel[ids[t][j]] >= sel[ids[t][j + 1]] - 2e-6 for j in range(k - 1)), f"token {t}"
+            close = np.abs(np.diff(sel[r["topk_ids"][t]])) < 2e-6
+            if not close.any():
+                assert list(ids[t]) == list(r["topk_ids"][t]), f"token {t}"
         else:
             kth = np.sort(r["sel"][t])[::-1][k - 1]
             assert all(r["sel"][t][e] >= kth - 2e-6 for e in gset), f"token {t}"
