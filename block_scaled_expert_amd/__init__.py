@@ -31,7 +31,7 @@ STAGES = ("quant_x", "dispatch", "gate_up", "quant_h", "down", "combine")
 EXPORTED = ("moe_status_string", "moe_check_arch", "moe_validate_config", "moe_workspace_size",
             "moe_quantize_act", "moe_route", "moe_dispatch", "moe_prepare_weights", "moe_forward",
             "moe_forward_fused", "moe_forward_fused_status", "moe_cap_swiglu", "moe_encode_weights",
-            "moe_decode_weights")
+            "moe_decode_weights", "moe_forward_noalloc", "moe_noalloc_scratch_bytes")
 LAYOUT_CANONICAL, LAYOUT_PACKED = 0, 1
 
 
@@ -83,9 +83,12 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, ctypes.POINTER(CWeights), vp, vp,
                                 sz, vp, vp]
     lib.moe_forward_fused.argtypes = lib.moe_forward.argtypes
+    lib.moe_forward_noalloc.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, ctypes.POINTER(CWeights), vp, vp]
+    lib.moe_noalloc_scratch_bytes.argtypes = []
     for name in EXPORTED:
         if name != "moe_status_string":
             getattr(lib, name).restype = ctypes.c_int
+    lib.moe_noalloc_scratch_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -333,3 +336,21 @@ def forward(cfg: Config, x, topk_ids, topk_w, weights, out, ws, events=None, fus
            _ptr(topk_w, torch.float32, (T, k), "topk_w"), ctypes.byref(cw),
            _ptr(out, torch.bfloat16, (T, H), "out"), _ptr(ws, torch.uint8, None, "ws"),
            ws.numel(), _stream(), ev), "moe_forward_fused" if fused else "moe_forward")
+
+
+def forward_noalloc(cfg: Config, x, topk_ids, topk_w, weights, out) -> None:
+    """moe_forward_noalloc: moe_forward with the library's per-device scratch
+    buffer as its workspace (no workspace argument, nothing allocated)."""
+    import torch
+    T = x.shape[0]
+    H, k = cfg.hidden, cfg.top_k
+    cw = weights if isinstance(weights, CWeights) else weights_struct(cfg, weights)
+    cc = cfg.c()
+    _ok(load().moe_forward_noalloc(ctypes.byref(cc), _ptr(x, torch.bfloat16, (T, H), "x"), T,
+                                   _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+                                   _ptr(topk_w, torch.float32, (T, k), "topk_w"), ctypes.byref(cw),
+                                   _ptr(out, torch.bfloat16, (T, H), "out"), _stream()), "moe_forward_noalloc")
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load().moe_noalloc_scratch_bytes())

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "launch.h"
@@ -124,6 +125,30 @@ ActGs act_gs_of(const moe_config* c, int site, float* scratch) {
   return a;
 }
 
+// Workspace of moe_forward_noalloc: a file-scope device array, one per GPU
+// the library runs on, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not the device array: host code only ever
+// uses the device address hipGetSymbolAddress returns for the current
+// device (scratch_ptr).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];   // per device, set once under g_scratch_mu
+
+// Device address of the current device's scratch array (nullptr on error).
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 bool test_fail_requested() {
   const char* v = std::getenv("MOE_FUSED_TEST_FAIL");
   return v != nullptr && v[0] == '1';
@@ -143,6 +168,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED_FORMAT: return "unsupported expert format";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_SCRATCH_TOO_SMALL: return "batch needs more than moe_forward_noalloc's 64 MiB scratch buffer";
     default: return "unknown status";
   }
 }
@@ -507,6 +533,25 @@ int moe_forward_fused(const moe_config* c, const void* x, int32_t T, const int32
                       const float* topk_w, const moe_expert_weights* w, void* out, void* ws, size_t ws_bytes,
                       void* stream, void* const* events) {
   return forward_impl(c, x, T, topk_ids, topk_w, w, out, ws, ws_bytes, stream, events, true);
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int moe_forward_noalloc(const moe_config* c, const void* x, int32_t T, const int32_t* topk_ids, const float* topk_w,
+                        const moe_expert_weights* w, void* out, void* stream) {
+  int st = moe_validate_config(c);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > c->max_tokens) return MOE_ERR_TOO_MANY_TOKENS;
+  if (T == 0) return MOE_OK;
+  // the workspace layout sized for this call's T, carved from the array
+  moe_config ct = *c;
+  ct.max_tokens = T;
+  if (layout(&ct, T).total > kScratchBytes) return MOE_ERR_SCRATCH_TOO_SMALL;
+  if ((st = device_check()) != MOE_OK) return st;
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return MOE_ERR_HIP;
+  return forward_impl(&ct, x, T, topk_ids, topk_w, w, out, ws, kScratchBytes, stream, nullptr, false);
 }
 
 int moe_forward_fused_status(const moe_config* c, int32_t T, const void* ws, size_t ws_bytes, int32_t* err,

@@ -64,7 +64,9 @@ enum moe_status {
   MOE_ERR_TOO_MANY_TOKENS = -4,    /* T > cfg->max_tokens */
   MOE_ERR_UNSUPPORTED_FORMAT = -5,
   MOE_ERR_LAUNCH = -6,             /* a kernel launch failed (hipGetLastError) */
-  MOE_ERR_HIP = -7                 /* another HIP runtime call failed */
+  MOE_ERR_HIP = -7,                /* another HIP runtime call failed */
+  MOE_ERR_SCRATCH_TOO_SMALL = -8   /* moe_forward_noalloc: the batch needs more
+                                      than its fixed scratch buffer */
 };
 
 enum moe_fmt { MOE_FMT_NVFP4 = 1, MOE_FMT_MXFP8 = 2 };
@@ -339,6 +341,34 @@ int moe_forward(const moe_config* cfg, const void* x, int32_t T, const int32_t* 
 int moe_forward_fused(const moe_config* cfg, const void* x, int32_t T, const int32_t* topk_ids,
                       const float* topk_w, const moe_expert_weights* weights, void* out,
                       void* ws, size_t ws_bytes, void* stream, void* const* events);
+
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and result (bit-identical to moe_forward),
+ * with the workspace taken from a buffer the library holds on each device
+ * instead of from the caller.  The caller still passes inputs and outputs.
+ *  - The buffer: a fixed device array of moe_noalloc_scratch_bytes() =
+ *    64 MiB, one per GPU the library runs on, kept until the process ends;
+ *    its address on a device is looked up once, on the first call there.
+ *  - A call needs the workspace moe_workspace_size reports for a config with
+ *    max_tokens = T; above 64 MiB it returns MOE_ERR_SCRATCH_TOO_SMALL
+ *    before enqueueing anything (at Inkling size, hidden 4608, FFN 2304,
+ *    384 experts, top-8: up to 269 tokens in NVFP4, 363 in MXFP8).
+ *    T > cfg->max_tokens is
+ *    MOE_ERR_TOO_MANY_TOKENS.
+ *  - No hipMalloc / hipFree or allocating call, no synchronization; every
+ *    call writes all of the buffer it later reads, so no contents need to
+ *    carry over between calls.
+ *  - All calls on one GPU share its buffer: calls that can overlap on one
+ *    GPU (different streams, different host threads without ordering)
+ *    race and corrupt each other's results.  Serialize them, e.g. on one
+ *    stream.
+ * No stage events.  Errors as moe_forward, plus MOE_ERR_SCRATCH_TOO_SMALL. */
+int moe_forward_noalloc(const moe_config* cfg, const void* x, int32_t T, const int32_t* topk_ids,
+                        const float* topk_w, const moe_expert_weights* weights, void* out, void* stream);
+
+/* Bytes of moe_forward_noalloc's per-device buffer (host only). */
+size_t moe_noalloc_scratch_bytes(void);
 
 /* Status of the last moe_forward_fused call on workspace ws (same cfg and
  * T): enqueues on `stream` a store of its error word to *err (device int32):

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     for n in ("moe_route", "moe_quantize_act", "moe_forward", "moe_forward_fused", "moe_dispatch",
               "moe_prepare_weights", "moe_workspace_size", "moe_status_string", "moe_check_arch",
               "moe_validate_config", "moe_encode_weights", "moe_decode_weights", "moe_forward_fused_status",
-              "moe_cap_swiglu"):
+              "moe_cap_swiglu", "moe_forward_noalloc", "moe_noalloc_scratch_bytes"):
         assert n in names
 
 
@@ -55,7 +55,7 @@ def test_check_arch(lib):
 
 
 def test_status_strings(lib):
-    for st in range(0, -8, -1):
+    for st in range(0, -9, -1):
         assert bse.status_string(st) != "unknown status"
     assert bse.status_string(-99) == "unknown status"
 
@@ -211,3 +211,15 @@ def test_alignment_checked_before_device(lib):
     assert lib.moe_forward_fused_status(r, 8, ws, n.value, ctypes.c_void_p(0x2002), None) == -1
     assert lib.moe_forward_fused_status(r, 8, ws, n.value - 1, ok, None) == -3
     assert lib.moe_forward_fused_status(r, 65, ws, n.value, ok, None) == -4
+
+
+def test_noalloc_host_checks(lib):
+    """moe_forward_noalloc rejects, before touching a device, a batch whose
+    workspace exceeds its fixed 64 MiB buffer, and T above max_tokens."""
+    assert lib.moe_noalloc_scratch_bytes() == 64 << 20
+    big = _cfg(max_tokens=1024).c()
+    assert lib.moe_forward_noalloc(ctypes.byref(big), None, 270, None, None, None, None, None) == -8
+    assert lib.moe_forward_noalloc(ctypes.byref(big), None, 1025, None, None, None, None, None) == -4
+    assert lib.moe_forward_noalloc(ctypes.byref(big), None, 0, None, None, None, None, None) == 0
+    assert lib.moe_forward_noalloc(ctypes.byref(big), None, -1, None, None, None, None, None) == -1
+    assert "64 MiB" in bse.status_string(-8)
