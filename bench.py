@@ -267,7 +267,8 @@ def make_state(w, layout: str):
     return st
 
 
-def measure(st, steps: int, warmup: int, fused: bool = False, graph: bool = False, flush: bool = False):
+def measure(st, steps: int, warmup: int, fused: bool = False, graph: bool = False, flush: bool = False,
+            route_forward: bool = False):
     """Warm-up, then the timed region of exactly `steps` steps (the gate/up
     kernel's HIP events recorded inside it), then `steps` more steps with an
     event pair around each (per-step median; with `flush`, a 1 GiB write
@@ -279,8 +280,11 @@ def measure(st, steps: int, warmup: int, fused: bool = False, graph: bool = Fals
     xt, wrt, bt, ws, ids, tw, out = (st[n] for n in ("xt", "wrt", "bt", "ws", "ids", "tw", "out"))
 
     def step(events=None):
-        bse.route(cfg, xt, wrt, bt, ids, tw, None, ws)
-        bse.forward(cfg, xt, ids, tw, cw, out, ws, events=events, fused=fused)
+        if route_forward:
+            bse.route_forward(cfg, xt, wrt, bt, ids, tw, None, cw, out, ws, events=events)
+        else:
+            bse.route(cfg, xt, wrt, bt, ids, tw, None, ws)
+            bse.forward(cfg, xt, ids, tw, cw, out, ws, events=events, fused=fused)
 
     for _ in range(warmup):
         step()
@@ -485,6 +489,10 @@ def main() -> int:
     ap.add_argument("--encode-experts", type=int, default=64)
     ap.add_argument("--fused", action="store_true",
                     help="moe_forward_fused: the expert half as one launch")
+    ap.add_argument("--route-forward", action="store_true",
+                    help="moe_route_forward: routing, x quantization and dispatch in one launch (small batches)")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="batch size other than the workload's (small-batch decode timings)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -508,12 +516,16 @@ def main() -> int:
     # measurements run back to back (drawing weights on the host between
     # them would leave the GPU idle, and its clocks low, just before a timed
     # region).
-    sub_keys = [] if (args.no_sub or args.workload != "decode_nvfp4") else list(SUB_WORKLOADS)
+    sub_keys = [] if (args.no_sub or args.workload != "decode_nvfp4" or args.tokens) else list(SUB_WORKLOADS)
     w = synth.WORKLOADS[args.workload]
+    if args.tokens:
+        import dataclasses
+        w = dataclasses.replace(w, tokens=args.tokens, name=f"{w.name} at {args.tokens} tokens")
     states = {}
     for key in sub_keys + [w.key]:
-        log(f"workload {key}: {synth.WORKLOADS[key].name}")
-        states[key] = make_state(synth.WORKLOADS[key], args.layout)
+        wl = w if key == w.key else synth.WORKLOADS[key]
+        log(f"workload {key}: {wl.name}")
+        states[key] = make_state(wl, args.layout)
     subs = {}
     for key in sub_keys:
         st = states.pop(key)
@@ -522,9 +534,12 @@ def main() -> int:
         del st
 
     st = states.pop(w.key)
-    res = measure(st, args.steps, args.warmup, fused=args.fused, graph=args.graph, flush=args.flush)
+    res = measure(st, args.steps, args.warmup, fused=args.fused, graph=args.graph, flush=args.flush,
+                  route_forward=args.route_forward)
     wk = work_of(st)
     rec = record_of(st, res, wk, args.layout, args.fused, args.graph)
+    if args.route_forward:
+        rec["config"]["launch"] += ", moe_route_forward (routing + x quantization + dispatch in one launch)"
     line = {"metric": METRIC, "value": rec.pop("value"), "unit": rec.pop("unit"), "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": rec.pop("ms_per_step"), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": rec.pop("dtype"),

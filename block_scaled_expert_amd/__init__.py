@@ -31,7 +31,7 @@ STAGES = ("quant_x", "dispatch", "gate_up", "quant_h", "down", "combine")
 EXPORTED = ("moe_status_string", "moe_check_arch", "moe_validate_config", "moe_workspace_size",
             "moe_quantize_act", "moe_route", "moe_dispatch", "moe_prepare_weights", "moe_forward",
             "moe_forward_fused", "moe_forward_fused_status", "moe_cap_swiglu", "moe_encode_weights",
-            "moe_decode_weights", "moe_forward_noalloc", "moe_noalloc_scratch_bytes")
+            "moe_decode_weights", "moe_forward_noalloc", "moe_noalloc_scratch_bytes", "moe_route_forward")
 LAYOUT_CANONICAL, LAYOUT_PACKED = 0, 1
 
 
@@ -85,6 +85,8 @@ def load() -> ctypes.CDLL:
     lib.moe_forward_fused.argtypes = lib.moe_forward.argtypes
     lib.moe_forward_noalloc.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, ctypes.POINTER(CWeights), vp, vp]
     lib.moe_noalloc_scratch_bytes.argtypes = []
+    lib.moe_route_forward.argtypes = [ctypes.POINTER(CConfig), vp, i32, vp, vp, vp, vp, vp, ctypes.POINTER(CWeights),
+                                      vp, vp, sz, vp, vp]
     for name in EXPORTED:
         if name != "moe_status_string":
             getattr(lib, name).restype = ctypes.c_int
@@ -354,3 +356,26 @@ def forward_noalloc(cfg: Config, x, topk_ids, topk_w, weights, out) -> None:
 
 def noalloc_scratch_bytes() -> int:
     return int(load().moe_noalloc_scratch_bytes())
+
+
+def route_forward(cfg: Config, x, w_router, bias, topk_ids, topk_w, near_tie, weights, out, ws, events=None) -> None:
+    """moe_route_forward: routing and the forward in one call; for small
+    batches routing, x quantization and dispatch are one launch."""
+    import torch
+    T = x.shape[0]
+    H, E, k = cfg.hidden, cfg.num_experts, cfg.top_k
+    cw = weights if isinstance(weights, CWeights) else weights_struct(cfg, weights)
+    ev = None
+    if events is not None:
+        if len(events) != 2 * len(STAGES):
+            raise ValueError("events must hold 2 per stage")
+        ev = (ctypes.c_void_p * len(events))(*[e.cuda_event if e is not None else None for e in events])
+    cc = cfg.c()
+    _ok(load().moe_route_forward(ctypes.byref(cc), _ptr(x, torch.bfloat16, (T, H), "x"), T,
+                                 _ptr(w_router, torch.bfloat16, (E, H), "w_router"),
+                                 _ptr(bias, torch.float32, (E,), "bias"),
+                                 _ptr(topk_ids, torch.int32, (T, k), "topk_ids"),
+                                 _ptr(topk_w, torch.float32, (T, k), "topk_w"),
+                                 _ptr(near_tie, torch.uint8, (T,), "near_tie"), ctypes.byref(cw),
+                                 _ptr(out, torch.bfloat16, (T, H), "out"), _ptr(ws, torch.uint8, None, "ws"),
+                                 ws.numel(), _stream(), ev), "moe_route_forward")

@@ -5,6 +5,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <random>
 
 #include "../../include/moe.h"
 #include "launch.h"
@@ -35,7 +36,7 @@ int n_local(const moe_config* c) { return c->num_local_experts; }
 
 // Workspace regions (byte offsets, each 256-byte aligned).
 struct Layout {
-  size_t z, xq, xs, xg, ags, counts, offsets, sorted, pos, work, ntiles, ctl, h, hq, hs, hg, y, total;
+  size_t z, xq, xs, xg, ags, counts, offsets, sorted, pos, work, ntiles, ctl, flags, h, hq, hs, hg, y, total;
   int max_tiles, nchunks;
 };
 
@@ -65,6 +66,7 @@ Layout layout(const moe_config* c, int T) {
   L.work = take((size_t)L.max_tiles * 2 * 4);
   L.ntiles = take(4);
   L.ctl = take((size_t)fused_ctl_words(L.max_tiles) * 4);
+  L.flags = take((size_t)route_prep_flag_words((int)E) * 8);   // moe_route_forward's completion flags
   L.h = take(nv ? P * F * 4 : 0);    // fp32 h: NVFP4 only (MXFP8 h is encoded by the gate/up epilogue)
   L.hq = take(P * (nv ? F / 2 : F));
   L.hs = take(P * (nv ? F / 16 : F / 32));
@@ -147,6 +149,29 @@ void* scratch_ptr() {
     g_scratch_ptr[dev] = p;
   }
   return g_scratch_ptr[dev];
+}
+
+// Per-call epochs for moe_route_forward's completion flags: distinct for
+// every call in the process and, through a random start, unlikely to match
+// anything a workspace held before.
+std::atomic<uint64_t> g_epoch{0};
+std::once_flag g_epoch_once;
+uint64_t next_epoch() {
+  std::call_once(g_epoch_once, [] {
+    std::random_device rd;
+    g_epoch.store(((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ 0x9E3779B97F4A7C15ull);
+  });
+  uint64_t e;
+  do e = g_epoch.fetch_add(1) + 1; while (e == 0);
+  return e;
+}
+
+// Whether moe_route_forward runs routing, x quantization and dispatch as
+// one launch: small batches (T <= 256, T k <= 4096) without a per-tensor
+// NVFP4 x scale (which needs its maximum before any row).
+bool route_forward_one_launch(const moe_config* c, int T) {
+  return T > 0 && T <= kRoutePrepMaxTokens && (long)T * c->top_k <= kSmallDispatchPairs &&
+         !(c->fmt == MOE_FMT_NVFP4 && c->act_gs == MOE_ACT_GS_PER_TENSOR);
 }
 
 bool test_fail_requested() {
@@ -365,7 +390,7 @@ int moe_prepare_weights(const moe_config* c, const moe_expert_weights* src, moe_
 
 static int forward_impl(const moe_config* c, const void* x, int32_t T, const int32_t* topk_ids,
                         const float* topk_w, const moe_expert_weights* w, void* out, void* ws, size_t ws_bytes,
-                        void* stream, void* const* events, bool fused) {
+                        void* stream, void* const* events, bool fused, bool prep_done = false) {
   int st = moe_validate_config(c);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
@@ -404,7 +429,9 @@ static int forward_impl(const moe_config* c, const void* x, int32_t T, const int
   fused = fused && fused_applies(c, T);
   float* const ags = at<float>(ws, L.ags);
   const ActGs agx = act_gs_of(c, 0, ags), agh = act_gs_of(c, 1, ags);
-  if (P <= kSmallDispatchPairs) {
+  if (prep_done) {
+    // x quantized and dispatched by moe_route_forward's first launch
+  } else if (P <= kSmallDispatchPairs) {
     // 1 + 2. quantize x per row and dispatch (+ tile list) in one launch; the
     // quantize-x stage covers both, the dispatch stage is empty
     record(events, 2 * MOE_STAGE_QUANT_X, s);
@@ -552,6 +579,70 @@ int moe_forward_noalloc(const moe_config* c, const void* x, int32_t T, const int
   void* ws = scratch_ptr();
   if (ws == nullptr) return MOE_ERR_HIP;
   return forward_impl(&ct, x, T, topk_ids, topk_w, w, out, ws, kScratchBytes, stream, nullptr, false);
+}
+
+int moe_route_forward(const moe_config* c, const void* x, int32_t T, const void* w_router, const float* bias,
+                      int32_t* topk_ids, float* topk_w, uint8_t* near_tie, const moe_expert_weights* w, void* out,
+                      void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  int st = moe_validate_config(c);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(c, T, ws, ws_bytes)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const bool nv = c->fmt == MOE_FMT_NVFP4;
+  const bool one_launch = route_forward_one_launch(c, T);
+  if (!one_launch) {
+    // larger batches: the router launches, then moe_forward's sequence
+    if ((st = moe_route(c, x, T, w_router, bias, topk_ids, topk_w, near_tie, ws, ws_bytes, stream)) != MOE_OK)
+      return st;
+    return forward_impl(c, x, T, topk_ids, topk_w, w, out, ws, ws_bytes, stream, events, false);
+  }
+  if (x == nullptr || w_router == nullptr || bias == nullptr || topk_ids == nullptr || topk_w == nullptr ||
+      w == nullptr || out == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(bias, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = device_check()) != MOE_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Layout L = layout(c, c->max_tokens);
+  RoutePrepArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.wr = static_cast<const uint16_t*>(w_router);
+  a.bias = bias;
+  a.T = T;
+  a.H = c->hidden;
+  a.E = c->num_experts;
+  a.k = c->top_k;
+  a.S = router_splits(T, c->num_experts);
+  a.norm_topk = c->norm_topk;
+  a.routed_scale = c->routed_scale;
+  a.z = at<float>(ws, L.z);
+  a.ids = topk_ids;
+  a.w = topk_w;
+  a.near_tie = near_tie;
+  a.xq = at<uint8_t>(ws, L.xq);
+  a.xs = at<uint8_t>(ws, L.xs);
+  a.xg = at<float>(ws, L.xg);
+  a.gs_val = (nv && c->act_gs == MOE_ACT_GS_STATIC) ? c->act_gs_static[0] : 1.0f;
+  a.E_begin = c->expert_begin;
+  a.E_local = c->num_local_experts;
+  a.tile_m = forward_tile_m(c, T);
+  a.d.counts = at<int32_t>(ws, L.counts);
+  a.d.offsets = at<int32_t>(ws, L.offsets);
+  a.d.sorted = at<int32_t>(ws, L.sorted);
+  a.d.pos = at<int32_t>(ws, L.pos);
+  a.d.worklist = at<int32_t>(ws, L.work);
+  a.d.ntiles = at<int32_t>(ws, L.ntiles);
+  a.flags = at<uint64_t>(ws, L.flags);
+  a.epoch = next_epoch();
+  record(events, 2 * MOE_STAGE_QUANT_X, s);
+  const int bad = launch_route_prep(a, c->fmt, (nv && c->act_gs == MOE_ACT_GS_STATIC) ? 2 : 0, s);
+  record(events, 2 * MOE_STAGE_QUANT_X + 1, s);
+  record(events, 2 * MOE_STAGE_DISPATCH, s);
+  record(events, 2 * MOE_STAGE_DISPATCH + 1, s);
+  if (bad) return MOE_ERR_LAUNCH;
+  return forward_impl(c, x, T, topk_ids, topk_w, w, out, ws, ws_bytes, stream, events, false, true);
 }
 
 int moe_forward_fused_status(const moe_config* c, int32_t T, const void* ws, size_t ws_bytes, int32_t* err,

@@ -64,6 +64,36 @@ int launch_prep_small(int fmt, const uint16_t* x, int T, int H, uint8_t* xq, uin
                       const int32_t* ids, int P, int E_begin, int E_local, int tile_m, const DispatchBufs& b,
                       int32_t* zero, int nzero, hipStream_t stream, const ActGs& ag = ActGs{});
 
+// Routing, quantization of the token rows and dispatch in one launch for
+// small batches (dispatch.hip): T <= kRoutePrepMaxTokens, T k <= 4096.
+constexpr int kRoutePrepMaxTokens = 256;
+struct RoutePrepArgs {
+  // router
+  const uint16_t* x;
+  const uint16_t* wr;
+  const float* bias;
+  int T, H, E, k, S, norm_topk;
+  float routed_scale;
+  float* z;                // router_splits(T, E) partial planes [S][T][E]
+  int32_t* ids;
+  float* w;
+  uint8_t* near_tie;       // nullable
+  // quantization (fmt 1: codes, scales, row scales; fmt 2: codes, scales)
+  uint8_t* xq;
+  uint8_t* xs;
+  float* xg;
+  float gs_val;            // static NVFP4 scale (gs mode 2)
+  // dispatch
+  int E_begin, E_local, tile_m;
+  DispatchBufs d;
+  // completion flags (route_prep_flag_words(E) uint64 words) and the call's epoch
+  uint64_t* flags;
+  uint64_t epoch;
+};
+int route_prep_flag_words(int E);
+// gs_mode: ActGs mode 0 (per row) or 2 (static); per-tensor scales are not supported here
+int launch_route_prep(const RoutePrepArgs& a, int fmt, int gs_mode, hipStream_t stream);
+
 // Weight encoding: nmat matrices [rows][cols] (dtype 0 bf16, 1 fp32) to
 // canonical NVFP4 (fmt 1: one fp32 scale per matrix, written to
 // gs[(m / gs_group) * gs_stride + m % gs_group]; amax: nmat words of device

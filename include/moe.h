@@ -342,6 +342,26 @@ int moe_forward_fused(const moe_config* cfg, const void* x, int32_t T, const int
                       const float* topk_w, const moe_expert_weights* weights, void* out,
                       void* ws, size_t ws_bytes, void* stream, void* const* events);
 
+/* moe_route followed by moe_forward, with routing, x quantization and
+ * dispatch in ONE launch for small batches (T <= 256 tokens and T * top_k
+ * <= 4096 pairs; NVFP4 with a per-tensor activation scale excepted), where
+ * the layer is bound by launches and the waits between them (TokenSpeed blog
+ * "TML Inkling 2 Small at Day 0", the paragraph after the "What's new"
+ * table; SGLang blog "SGLang and Miles Add Day-0 Support for Inkling 2
+ * Small", "Performance").  The expert half follows as in moe_forward.
+ * Arguments: those of moe_route and moe_forward together.  Results
+ * (topk_ids, topk_w, near_tie, out) are bit-identical to moe_route +
+ * moe_forward.  Inside the one launch, work items wait for earlier ones
+ * through completion flags tagged with a per-call value, so the workspace
+ * still needs no initial contents; each wait is bounded (reaching the bound
+ * needs a device fault elsewhere), and a token whose routing wait ran out
+ * gets NaN gate weights and a NaN output row.  Larger batches run moe_route's
+ * and moe_forward's launches.  events: the QUANT_X pair times the one
+ * launch, the DISPATCH pair is empty; the other stages as in moe_forward. */
+int moe_route_forward(const moe_config* cfg, const void* x, int32_t T, const void* w_router, const float* bias,
+                      int32_t* topk_ids, float* topk_w, uint8_t* near_tie, const moe_expert_weights* weights,
+                      void* out, void* ws, size_t ws_bytes, void* stream, void* const* events);
+
 /* moe_forward for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same computation, kernels and result (bit-identical to moe_forward),
