@@ -22,9 +22,9 @@ pytestmark = pytest.mark.gpu
 # ------------------------------------------------------------------ router --
 # Router kernel variants by batch: split-K GEMV tiles of 16 / 32 / 64 tokens
 # with 6 / 4 / 2 K slices up to 256 tokens, then 128 x 128 LDS tiles with as
-# many K slices as keep one round of workgroups (6 at 300 and 2048 tokens, 5
-# at 4096 -- slices of 14 and 15 steps, the odd last step skipped -- 1 at
-# 16384); top-k with 1 / 2 / 4 / 8 / 16 experts per lane.
+# many K slices as keep the grid within 256 workgroups, at least 2 (6 at 300
+# tokens; 5 at 2048 -- slices of 14 and 15 steps, the odd last step skipped;
+# 2 at 4096 and 16384); top-k with 1 / 2 / 4 / 8 / 16 experts per lane.
 ROUTER_CASES = [
     (24, 384, 8), (100, 384, 8), (200, 384, 8), (300, 384, 8), (2048, 384, 8), (4096, 384, 8),
     (50, 40, 4), (130, 100, 6), (37, 200, 8), (300, 600, 8), (70, 1000, 8), (5, 64, 3),
