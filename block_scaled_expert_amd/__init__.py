@@ -3,11 +3,13 @@
 Argument marshalling only: every step of the layer runs in the library's HIP
 kernels on the caller's current torch stream.  The functions mirror the C
 ABI in include/moe.h (moe_route, moe_dispatch, moe_quantize_act,
-moe_forward, moe_forward_fused, moe_forward_fused_status, moe_cap_swiglu,
-moe_workspace_size, moe_check_arch, moe_status_string, the weight encoder
-and decoder).
-Tensors must be contiguous and on the current CUDA (HIP) device; the library
-never allocates, so callers pass outputs and a workspace.
+moe_forward, moe_forward_fused, moe_forward_fused_status, moe_route_forward,
+moe_forward_noalloc, moe_cap_swiglu, moe_workspace_size,
+moe_noalloc_scratch_bytes, moe_check_arch, moe_status_string, the weight
+encoder and decoder).
+Tensors must be contiguous and on the current CUDA (HIP) device; apart from
+moe_forward_noalloc's fixed device array the library never allocates, so
+callers pass outputs and a workspace.
 
 There is no fallback: if the built library is missing, load() raises.
 """

@@ -254,3 +254,15 @@ def test_expert_matches_plain_f64_ffn_on_representable_inputs():
     assert np.array_equal(h, href)
     hq = F.dequantize_mxfp8(*F.quantize_mxfp8(h))
     assert np.array_equal(y, (torch.from_numpy(hq) @ torch.from_numpy(D).T).float().numpy())
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+def test_worker_pool_matches_one_process(fmt):
+    """Experts evaluated by forked worker processes give the serial result bit
+    for bit (the per-expert arithmetic is unchanged; the combine is a
+    fixed-order sum)."""
+    cfg, x, wr, b, ws = _small(seed=16, E=12, k=3, fmt=fmt)
+    one = L.moe_layer(cfg, x, wr, b, ws)
+    pool = L.moe_layer(cfg, x, wr, b, ws, workers=3)
+    for key in ("out", "y", "topk_ids", "topk_w"):
+        assert np.array_equal(np.asarray(one[key]).view(np.uint8), np.asarray(pool[key]).view(np.uint8)), key
