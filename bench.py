@@ -52,6 +52,24 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5) -> None:
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
+def expert_shapes(w, n: int) -> dict:
+    """Byte shapes of n local experts' canonical arrays: gate and up rows then
+    down rows, NVFP4 (two E2M1 codes per byte, one E4M3 scale per 16) or
+    MXFP8 (one E4M3 code per byte, one E8M0 scale per 32)."""
+    H, F = w.hidden, w.ffn
+    nv = w.fmt == "nvfp4"
+    return {"w13": (n, 2 * F, H // 2 if nv else H), "w13_sc": (n, 2 * F, H // (16 if nv else 32)),
+            "w2": (n, H, F // 2 if nv else F), "w2_sc": (n, H, F // (16 if nv else 32))}
+
+
+def per_expert_bytes(w) -> dict:
+    """Bytes of one expert by array (the algorithmic bytes of the roofline),
+    with the NVFP4 per-matrix fp32 scales (gate, up, down) under "gs"."""
+    b = {k: int(np.prod(s[1:])) for k, s in expert_shapes(w, 1).items()}
+    b["gs"] = 12 if w.fmt == "nvfp4" else 0
+    return b
+
+
 def upload_weights(w, bse_cfg):
     """Generate the local experts' direct-code weights and copy them to HBM."""
     import torch
@@ -59,8 +77,7 @@ def upload_weights(w, bse_cfg):
     n = bse_cfg.num_local
     H, F = w.hidden, w.ffn
     nv = w.fmt == "nvfp4"
-    shapes = {"w13": (n, 2 * F, H // 2 if nv else H), "w13_sc": (n, 2 * F, H // (16 if nv else 32)),
-              "w2": (n, H, F // 2 if nv else F), "w2_sc": (n, H, F // (16 if nv else 32))}
+    shapes = expert_shapes(w, n)
     dev = {k: torch.empty(s, dtype=torch.uint8, device="cuda") for k, s in shapes.items()}
     gs = np.zeros((n, 3), dtype=np.float32)
     for i in range(n):
@@ -71,9 +88,7 @@ def upload_weights(w, bse_cfg):
             gs[i] = ew["gs"]
     if nv:
         dev["gs"] = torch.from_numpy(gs).cuda()
-    per_expert = {k: int(np.prod(s[1:])) for k, s in shapes.items()}
-    per_expert["gs"] = 12 if nv else 0
-    return dev, per_expert
+    return dev, per_expert_bytes(w)
 
 
 def gemm_source(workload: str) -> str:
@@ -140,7 +155,7 @@ class _CachedExperts:
 
 def host_cores() -> int:
     """CPU cores this process may use: its affinity set, capped by
-    OMP_NUM_THREADS when that is set (the CPU share of a GPU machine)."""
+    OMP_NUM_THREADS when that is set (the CPU share of a shared machine)."""
     n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     omp = os.environ.get("OMP_NUM_THREADS")
     if omp and omp.isdigit() and int(omp) > 0:
@@ -496,8 +511,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the layer is measured on one GPU's "
-              f"share, see DESIGN.md for how it would shard.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the layer is measured on one GPU's "
+              f"share (the EP8 workload is one expert-parallel rank's experts); no multi-GPU path is built.",
+              file=sys.stderr)
         return 2
 
     import torch

@@ -11,7 +11,7 @@ row).  The definitions below are the public conventions those names refer to:
 * E8M0: unsigned power of two 2^(c-127) for c = 0..254; 255 (NaN) never
   produced.
 
-Readings where the pages are silent (each also stated in the design doc):
+Readings where the pages are silent (numbered R1, R2, ... throughout this package):
 
 * R3 (MX scale): X = 2^(floor(log2 amax) - 8), 8 being the E4M3 emax; the
   exponent is clamped to [-127, 127]; elements saturate to +-448.

@@ -16,7 +16,7 @@ row; Miles docs section 1, "Sigmoid-routed MoE" bullet; SGLang blog
    projection.
 6. Weighted combine of the k expert outputs per token.
 
-Readings taken where the pages are silent (numbered as in the design doc):
+Readings taken where the pages are silent (numbered R1, R2, ... throughout this package):
 
 * R6  bias enters the selection only; gate weights use the plain sigmoid.
 * R7  norm_topk (default on): gate weights are divided by their sum over the
