@@ -18,11 +18,13 @@ pytestmark = pytest.mark.gpu
 
 
 def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None, layout="packed", fused=False, act=None,
-              expect_fused_err=0):
+              expect_fused_err=0, x=None):
     """act: optional (act_gs mode, (x scale, h scale)) for NVFP4 activations.
-    fused: moe_forward_fused, whose status word must equal expect_fused_err."""
+    fused: moe_forward_fused, whose status word must equal expect_fused_err.
+    x: optional bf16 token rows (bits) in place of the workload's."""
     import torch
-    x, wr, b = inputs(w, T)
+    x0, wr, b = inputs(w, T)
+    x = x0 if x is None else x
     T = x.shape[0]
     kw = {} if cap_form is None else {"cap_form": cap_form}
     if act is not None:
@@ -126,6 +128,26 @@ def test_large_m_partial_tiles_every_subtile_count(gpu_lib, fmt):
     rem = np.bincount(r["ids"].ravel(), minlength=w.experts) % 128
     assert set(int(v) for v in np.ceil(rem[rem > 0] / 16)) == set(range(1, 9))
     assert rel_err(r["out"], oracle_out(w, r)) <= OUT_RTOL
+
+
+# Per-row activation scales and per-row GEMM arithmetic: a token's output
+# does not depend on the other tokens of the batch.  At one batch size (so
+# the same kernels and tile heights) replacing two of every three tokens
+# leaves the kept tokens' rows bit-identical, although the dispatch places
+# them at other positions of other tiles.
+@pytest.mark.parametrize("key", ["decode_nvfp4", "ragged_mxfp8", "ragged_nvfp4"])
+def test_token_rows_independent_of_the_rest_of_the_batch(gpu_lib, key):
+    ragged = {w.key: w for w in RAGGED.values()}
+    w = ragged.get(key) or synth.WORKLOADS[key]
+    a = run_layer(gpu_lib, w)
+    x2 = a["x"].copy()
+    other = np.arange(w.tokens) % 3 != 0
+    x2[other] = synth.tokens(w.seed + 1000, w.tokens, w.hidden)[other]
+    b = run_layer(gpu_lib, w, x=x2)
+    kept = ~other
+    assert np.array_equal(a["ids"][kept], b["ids"][kept])
+    assert not np.array_equal(a["ids"][other], b["ids"][other])
+    assert np.array_equal(a["out"][kept], b["out"][kept])
 
 
 def test_single_token_and_max_tokens_margin(gpu_lib):
