@@ -18,10 +18,11 @@ pytestmark = pytest.mark.gpu
 
 
 def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None, layout="packed", fused=False, act=None,
-              expect_fused_err=0, x=None):
+              expect_fused_err=0, x=None, ids=None, tw=None):
     """act: optional (act_gs mode, (x scale, h scale)) for NVFP4 activations.
     fused: moe_forward_fused, whose status word must equal expect_fused_err.
-    x: optional bf16 token rows (bits) in place of the workload's."""
+    x: optional bf16 token rows (bits) in place of the workload's.
+    ids, tw: optional routing to replay (moe_route is then not called)."""
     import torch
     x0, wr, b = inputs(w, T)
     x = x0 if x is None else x
@@ -35,13 +36,19 @@ def run_layer(bse, w, gain=1.0, T=None, cap_form=None, max_tokens=None, layout="
     if layout == "packed":
         wd = bse.prepare_weights(cfg, wd)
     ws = bse.workspace(cfg)
-    ids = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
-    tw = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
+    replay = ids is not None
+    if replay:
+        ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+        tw = torch.from_numpy(np.ascontiguousarray(tw, dtype=np.float32)).cuda()
+    else:
+        ids = torch.empty((T, w.top_k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((T, w.top_k), dtype=torch.float32, device="cuda")
     nt = torch.empty(T, dtype=torch.uint8, device="cuda")
     xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
     wrt = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).cuda()
     out = torch.empty((T, w.hidden), dtype=torch.bfloat16, device="cuda")
-    bse.route(cfg, xt, wrt, torch.from_numpy(b).cuda(), ids, tw, nt, ws)
+    if not replay:
+        bse.route(cfg, xt, wrt, torch.from_numpy(b).cuda(), ids, tw, nt, ws)
     bse.forward(cfg, xt, ids, tw, wd, out, ws, fused=fused)
     fused_err = None
     if fused:   # the single launch's error word: every dependency wait met
@@ -148,6 +155,31 @@ def test_token_rows_independent_of_the_rest_of_the_batch(gpu_lib, key):
     assert np.array_equal(a["ids"][kept], b["ids"][kept])
     assert not np.array_equal(a["ids"][other], b["ids"][other])
     assert np.array_equal(a["out"][kept], b["out"][kept])
+
+
+def _bf16_f64(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("key", ["mid_nvfp4", "mid_mxfp8"])
+def test_topk_slot_permutation_changes_only_the_combine_rounding(gpu_lib, key):
+    """Replaying the routing with each token's k slots permuted: every pair's
+    expert output is the same, and the combine sums the same products in
+    another fp32 order, so each output element moves by at most one bf16 step
+    (plus fp32 reordering error where terms cancel), and the oracle bar
+    holds."""
+    w = SMALL[key]
+    a = run_layer(gpu_lib, w)
+    g = np.random.default_rng(9)
+    perm = np.stack([g.permutation(w.top_k) for _ in range(w.tokens)])
+    b = run_layer(gpu_lib, w, ids=np.take_along_axis(a["ids"], perm, 1), tw=np.take_along_axis(a["tw"], perm, 1))
+    fa, fb = _bf16_f64(a["out"]), _bf16_f64(b["out"])
+    # one bf16 step of the larger value, plus a small absolute slack for
+    # elements whose terms cancel (fp32 reordering error of the products)
+    bound = np.maximum(np.abs(fa), np.abs(fb)) * 2.0 ** -7 + np.abs(fa).max() * 2.0 ** -16
+    assert np.all(np.abs(fa - fb) <= bound)
+    assert not np.array_equal(a["ids"], b["ids"])
+    assert rel_err(b["out"], oracle_out(w, b)) <= OUT_RTOL
 
 
 def test_single_token_and_max_tokens_margin(gpu_lib):

@@ -266,3 +266,19 @@ def test_worker_pool_matches_one_process(fmt):
     pool = L.moe_layer(cfg, x, wr, b, ws, workers=3)
     for key in ("out", "y", "topk_ids", "topk_w"):
         assert np.array_equal(np.asarray(one[key]).view(np.uint8), np.asarray(pool[key]).view(np.uint8)), key
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+def test_topk_slot_permutation_invariance(fmt):
+    """Permuting each token's k slots (ids and gate weights together) leaves
+    the layer output unchanged: the combine is a sum over the chosen experts
+    (accumulated in float64, rounded once to bf16)."""
+    cfg, x, wr, b, ws = _small(seed=17, E=12, k=4, fmt=fmt)
+    r = L.moe_layer(cfg, x, wr, b, ws)
+    g = np.random.default_rng(5)
+    perm = np.stack([g.permutation(cfg.top_k) for _ in range(x.shape[0])])
+    ids = np.take_along_axis(r["topk_ids"], perm, axis=1)
+    tw = np.take_along_axis(r["topk_w"], perm, axis=1)
+    p = L.moe_layer(cfg, x, wr, b, ws, topk_ids=ids, topk_w=tw)
+    assert not np.array_equal(ids, r["topk_ids"])
+    assert np.array_equal(p["out"], r["out"])
